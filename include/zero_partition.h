@@ -1,0 +1,258 @@
+/*
+ * zero_partition.h -- C ABI of libzero_partition.so: one rank's share of a
+ * ZeRO-DP optimizer step on an MI355X (gfx950).
+ *
+ * The method is described on the ZeRO explainer page ("ZeRO: Memory
+ * Optimizations Toward Training Trillion Parameter Models", azimuth.plus):
+ *   - model-states paragraph: per parameter the model states are an fp16
+ *     parameter (2 bytes), an fp16 gradient (2 bytes) and an fp32 Adam state
+ *     of master copy, momentum and variance (12 bytes), 16 bytes in all;
+ *   - Stage 1 (P_os), Stage 2 (P_os+g) and Stage 3 (P_os+g+p) paragraphs:
+ *     which of those kinds each of the N ranks keeps only 1/N of, that a
+ *     rank reduces only its own gradient slice (reduce-scatter), updates only
+ *     its own partition, and that the updated fp16 parameters are gathered
+ *     from every rank afterwards;
+ *   - constant-size buffers paragraph (ZeRO-R): small tensors are fused into
+ *     one fixed-size buffer that does not grow with the model.
+ *
+ * Conventions
+ *   - Every function returns ZERO_OK (0) or a negative zero_status.  A
+ *     thread-local message for the last error is in zero_last_error().
+ *   - Arguments are checked before anything is launched or written; on an
+ *     argument error no host or device state is modified.  After a
+ *     ZERO_ERR_HIP the device state reached by the failed call is undefined.
+ *   - fp16 values cross the ABI as uint16_t bit patterns (IEEE binary16).
+ *   - "device" pointers point into GPU memory of the current HIP device;
+ *     "host" pointers into ordinary host memory.  The caller owns every
+ *     buffer it passes; the library keeps no pointer beyond the call except
+ *     the tensor table given to zero_layout_bind_tensors.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is ordered on that stream.
+ *   - Flat indices and sizes are int64_t.
+ */
+#ifndef ZERO_PARTITION_H
+#define ZERO_PARTITION_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_PARTITION_VERSION 10000 /* 1.0.0 */
+
+typedef enum zero_status {
+    ZERO_OK = 0,
+    ZERO_ERR_INVALID_ARG = -1,    /* a null pointer, a size or index out of range */
+    ZERO_ERR_ALIGNMENT = -2,      /* a device pointer lacks the required alignment */
+    ZERO_ERR_CAPACITY = -3,       /* an output array is too small; the needed count is reported */
+    ZERO_ERR_INDEX_OVERFLOW = -4, /* a size or byte count does not fit in int64 */
+    ZERO_ERR_HIP = -5,            /* a HIP runtime call failed; see zero_last_hip_error() */
+    ZERO_ERR_OUT_OF_MEMORY = -6,  /* host or device allocation failed, or a table would be too large */
+    ZERO_ERR_STATE = -7           /* call not valid in this state (e.g. pack before bind) */
+} zero_status;
+
+/* ------------------------------------------------------------------------ */
+/* Partition layout (host only; no device work)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Opaque layout handle, created by zero_partition_layout and freed by
+ * zero_layout_destroy. */
+typedef struct zero_layout zero_layout;
+
+/* Summary of a layout.  Per-rank byte counts follow the model-states
+ * paragraph (2 + 2 + 4 + 4 + 4 bytes per element) and the stage paragraphs:
+ *   stage 0  nothing partitioned (plain data parallelism): every kind over Psi
+ *   stage 1  master, momentum, variance over S; fp16 param and grad over Psi
+ *   stage 2  additionally the fp16 gradient over S
+ *   stage 3  additionally the fp16 parameter over S
+ * Replicated kinds count the unpadded Psi, partitioned kinds the padded S. */
+typedef struct zero_layout_info {
+    int64_t psi;             /* total elements, sum of numel */
+    int64_t shard_elems;     /* S = roundup(ceil(psi / n_ranks), align_elems) */
+    int64_t padded_elems;    /* n_ranks * S */
+    int64_t padding;         /* padded_elems - psi */
+    int64_t n_tensors;
+    int64_t align_elems;
+    int64_t bucket_elems;    /* B; 0 when no bucket plan */
+    int64_t n_fills;         /* ceil(psi / B); 0 when B == 0 */
+    int64_t n_segments;
+    int32_t n_ranks;
+    int32_t stage;
+    int64_t bytes_param16;   /* per-rank bytes of each kind at this stage */
+    int64_t bytes_grad16;
+    int64_t bytes_master;
+    int64_t bytes_momentum;
+    int64_t bytes_variance;
+    int64_t bytes_total;
+} zero_layout_info;
+
+/* One piece of a tensor that lies inside one shard (and, with a bucket plan,
+ * inside one bucket fill).  Segments are sorted by flat_off and tile
+ * [0, psi) exactly; zero-sized tensors have no segment. */
+typedef struct zero_segment {
+    int32_t tensor;      /* index in the tensor list */
+    int32_t owner;       /* rank owning this piece: flat_off / S */
+    int64_t tensor_off;  /* element offset inside the tensor */
+    int64_t flat_off;    /* element offset in the flattened vector */
+    int64_t len;         /* elements, > 0 */
+    int64_t shard_off;   /* flat_off - owner * S */
+    int64_t fill;        /* flat_off / B, or -1 without a bucket plan */
+    int64_t bucket_off;  /* flat_off - fill * B, or -1 without a bucket plan */
+} zero_segment;
+
+/* Build the layout of a list of tensors flattened in list order (no
+ * per-tensor padding) and cut into n_ranks equal shards of S elements.
+ *   numel        host, n_tensors sizes (>= 0); may be NULL when n_tensors == 0
+ *   n_ranks      N >= 1
+ *   stage        0..3 (which kinds are partitioned, for the byte counts)
+ *   align_elems  A >= 1: S is a multiple of A
+ *   bucket_elems B >= 0: with B > 0 segments are also cut at multiples of B
+ *                (the fills of the constant-size bucket)
+ *   out          receives the new handle
+ * Errors: INVALID_ARG (ranges), INDEX_OVERFLOW (sum of sizes, or 16 * N * S
+ * bytes, beyond int64), OUT_OF_MEMORY (more than 2^26 segments). */
+int zero_partition_layout(const int64_t* numel, int64_t n_tensors, int32_t n_ranks,
+                          int32_t stage, int64_t align_elems, int64_t bucket_elems,
+                          zero_layout** out);
+
+int zero_layout_destroy(zero_layout* layout); /* NULL is accepted; frees device tables too */
+
+int zero_layout_get_info(const zero_layout* layout, zero_layout_info* info);
+
+/* Flat offset of every tensor (host, n_tensors entries).  CAPACITY when
+ * cap < n_tensors. */
+int zero_layout_tensor_offsets(const zero_layout* layout, int64_t* out, int64_t cap);
+
+/* Rank r owns [begin, end); [begin, real_end) are model elements and
+ * [real_end, end) padding.  INVALID_ARG unless 0 <= rank < n_ranks. */
+int zero_layout_rank_range(const zero_layout* layout, int32_t rank,
+                           int64_t* begin, int64_t* real_end, int64_t* end);
+
+/* Segment queries.  *n_out always receives the number of matching segments;
+ * they are written to out (host) when cap is large enough, otherwise the call
+ * returns CAPACITY and writes nothing (call with cap = 0 to size the array). */
+int zero_layout_segments(const zero_layout* layout, zero_segment* out, int64_t cap,
+                         int64_t* n_out);
+int zero_layout_rank_segments(const zero_layout* layout, int32_t rank, zero_segment* out,
+                              int64_t cap, int64_t* n_out);
+int zero_layout_fill_segments(const zero_layout* layout, int64_t fill, zero_segment* out,
+                              int64_t cap, int64_t* n_out);
+
+/* ------------------------------------------------------------------------ */
+/* Bucket pack (constant-size buffers paragraph)                             */
+/* ------------------------------------------------------------------------ */
+
+/* Record the device address of every tensor of the layout and upload the
+ * gather tables the pack kernel reads (on the current device, ordered on
+ * `stream`; the call waits for the upload).
+ *   dev_ptrs  host array of n_tensors device pointers to fp16 data, each
+ *             2-byte aligned; NULL entries are allowed for zero-sized tensors.
+ * The tensors must stay allocated while the layout is used for packing.
+ * Binding again replaces the previous table.  Errors: STATE (layout has no
+ * bucket plan), INVALID_ARG, ALIGNMENT, HIP, OUT_OF_MEMORY. */
+int zero_layout_bind_tensors(zero_layout* layout, const uint16_t* const* dev_ptrs,
+                             void* stream);
+
+/* Write fill `fill` of the bucket: bucket[j] = flat[fill * B + j] for
+ * fill * B + j < psi and 0x0000 past the end, where flat is the concatenation
+ * of the bound tensors in list order.  A bit copy (NaN payloads, -0 kept).
+ *   bucket        device, B elements, 16-byte aligned
+ *   packed_elems  optional host output: min(B, psi - fill * B)
+ * Asynchronous on `stream`; must run on the device the layout was bound on.
+ * Errors: STATE (not bound, or another device), INVALID_ARG (fill outside
+ * [0, n_fills)), ALIGNMENT, HIP. */
+int zero_pack_bucket(const zero_layout* layout, int64_t fill, uint16_t* bucket,
+                     void* stream, int64_t* packed_elems);
+
+/* ------------------------------------------------------------------------ */
+/* Fused shard step (Stage 1/2/3 paragraphs: the rank's own partition)        */
+/* ------------------------------------------------------------------------ */
+
+/* fp32 shard state of one rank.  Set [cur] is the live state.  When
+ * p[1], m[1] and v[1] are all NULL the step runs in place (two passes over
+ * the gradients: an overflow check, then the update).  When all three are
+ * given the step reads set [cur] and writes set [1 - cur] in one pass, and
+ * a taken step flips `cur` (ping-pong mode).  All six pointers are device
+ * pointers to shard_elems floats, 16-byte aligned, and the sets may not
+ * overlap. */
+typedef struct zero_shard_state {
+    int64_t shard_elems;   /* S */
+    float* p[2];           /* fp32 master parameters */
+    float* m[2];           /* fp32 momentum (first moment) */
+    float* v[2];           /* fp32 variance (second moment) */
+    int32_t cur;           /* live set: 0 or 1 (always 0 in place) */
+    int32_t reserved;
+    int64_t t;             /* Adam steps taken so far (skipped steps excluded) */
+} zero_shard_state;
+
+typedef struct zero_adam_hparams {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;    /* L2 term added to the gradient; 0 disables it */
+} zero_adam_hparams;
+
+/* Dynamic loss scale.  A step is skipped when any reduced gradient value is
+ * inf or NaN: then scale = max(scale * backoff, min_scale), good_steps = 0
+ * and no state changes.  A taken step increments good_steps, and when it
+ * reaches growth_interval (> 0) the scale is multiplied by growth and
+ * good_steps reset. */
+typedef struct zero_loss_scaler {
+    float scale;           /* the contributions were multiplied by this */
+    float backoff;
+    float growth;
+    float min_scale;
+    int32_t growth_interval;
+    int32_t good_steps;
+} zero_loss_scaler;
+
+/* One rank's shard step:
+ *   sum   = grads[0] + grads[1] + ... + grads[R-1]   (fp16 inputs, fp32
+ *           additions in that order)
+ *   flag  = any element of sum is inf or NaN (over all S elements)
+ *   if flag: skip (no state change), scaler backs off
+ *   else, with t = st->t + 1:
+ *     g = sum * (1 / scale) [+ weight_decay * p]
+ *     m = beta1 * m + (1 - beta1) * g
+ *     v = beta2 * v + (1 - beta2) * g * g
+ *     p = p - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *     out_slot = fp16(p), round to nearest even
+ *     st->t = t, scaler counts a good step
+ *   grads     host array of R device pointers to S fp16 values each,
+ *             16-byte aligned (the R contributions to this rank's slice)
+ *   R         1..16
+ *   out_slot  device, S fp16 values, 2-byte aligned: this rank's slot of the
+ *             gather buffer (gather + rank * S)
+ *   overflow  host output: 1 if the step was skipped, else 0 (may be NULL)
+ * The call blocks until the overflow decision is known (it reads 4 bytes back
+ * and waits for `stream`); any work it enqueues after that (restoring the
+ * slot of a skipped ping-pong step) is ordered on `stream`.  Calls on one
+ * device are serialised by the library.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
+                    const zero_adam_hparams* hp, zero_loss_scaler* scaler,
+                    uint16_t* out_slot, void* stream, int32_t* overflow);
+
+/* ------------------------------------------------------------------------ */
+/* Misc                                                                      */
+/* ------------------------------------------------------------------------ */
+
+int zero_version(void);
+const char* zero_last_error(void);     /* thread-local, never NULL */
+int zero_last_hip_error(void);         /* hipError_t of the last ZERO_ERR_HIP */
+
+/* sizeof of the ABI structs, for binding checks: 0 layout_info, 1 segment,
+ * 2 shard_state, 3 adam_hparams, 4 loss_scaler; -1 otherwise. */
+int64_t zero_abi_struct_size(int32_t which);
+
+/* Architecture of the current device as a number (gfx950 -> 950) and its
+ * memory size in bytes. */
+int zero_device_info(int32_t* arch, int64_t* hbm_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_PARTITION_H */

@@ -166,8 +166,10 @@ class LossScaler:
             self.good_steps = 0
         else:
             self.good_steps += 1
-            if self.growth_interval > 0 and self.good_steps == self.growth_interval:
-                self.scale = float(np.float32(self.scale * self.growth))
+            if self.growth_interval > 0 and self.good_steps >= self.growth_interval:
+                grown = np.float32(self.scale * self.growth)
+                if np.isfinite(grown):
+                    self.scale = float(grown)
                 self.good_steps = 0
 
 

@@ -1,0 +1,301 @@
+// capi.cpp -- C ABI glue: errors, per-device workspace, the shard step's host
+// control (argument checks, Adam constants, overflow decision, loss scale).
+//
+// The step follows the Stage 1/2 paragraphs of the ZeRO explainer page
+// ("ZeRO: Memory Optimizations Toward Training Trillion Parameter Models",
+// azimuth.plus): the rank sums the gradient contributions of its own slice,
+// updates its own partition of the fp32 Adam state and writes its fp16
+// parameters into its slot of the gather buffer.  The skip-on-overflow loss
+// scaling around it is not on the page (standard mixed-precision practice).
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+#include <memory>
+#include <mutex>
+#include <string>
+
+#include "zp_internal.hpp"
+
+namespace zp {
+
+namespace {
+thread_local std::string g_last_error;
+thread_local int g_last_hip_error = 0;
+}  // namespace
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int fail_hip(hipError_t err, const char* what) {
+    g_last_hip_error = int(err);
+    g_last_error = std::string(what) + ": " + hipGetErrorString(err);
+    return ZERO_ERR_HIP;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    const long v = std::strtol(s, nullptr, 10);
+    if (v < lo || v > hi) return dflt;
+    return int(v);
+}
+
+}  // namespace
+
+int blocks_per_cu_step() {
+    static const int v = env_int("ZERO_BLOCKS_PER_CU", 8, 1, 64);
+    return v;
+}
+
+int blocks_per_cu_pack() {
+    static const int v = env_int("ZERO_PACK_BLOCKS_PER_CU", 8, 1, 64);
+    return v;
+}
+
+namespace {
+
+// Per-device workspace: the overflow flag word and a pinned host word to read
+// it back into.  Created on a device's first shard step and kept until the
+// process ends; `mu` serialises shard steps on the device (they share the
+// flag word).
+struct DeviceWorkspace {
+    std::mutex mu;
+    uint32_t* d_flag = nullptr;
+    uint32_t* h_flag = nullptr;
+    uint32_t epoch = 0;
+    int cu_count = 0;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mu;
+DeviceWorkspace* g_ws[kMaxDevices] = {};
+
+int get_workspace(int dev, DeviceWorkspace** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_ERR_INVALID_ARG, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (!g_ws[dev]) {
+        std::unique_ptr<DeviceWorkspace> ws(new (std::nothrow) DeviceWorkspace());
+        if (!ws) return fail(ZERO_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+        hipError_t e = hipDeviceGetAttribute(&ws->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+        e = hipMalloc(reinterpret_cast<void**>(&ws->d_flag), 256);
+        if (e != hipSuccess) return fail_hip(e, "hipMalloc (flag)");
+        e = hipMemset(ws->d_flag, 0, 256);
+        if (e == hipSuccess)
+            e = hipHostMalloc(reinterpret_cast<void**>(&ws->h_flag), 64, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            (void)hipFree(ws->d_flag);
+            return fail_hip(e, "workspace set-up");
+        }
+        *ws->h_flag = 0;
+        g_ws[dev] = ws.release();
+    }
+    *out = g_ws[dev];
+    return ZERO_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool finite_f(float x) { return std::isfinite(x); }
+
+}  // namespace
+}  // namespace zp
+
+using zp::fail;
+
+extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
+                               const zero_adam_hparams* hp, zero_loss_scaler* sc,
+                               uint16_t* out_slot, void* stream, int32_t* overflow) {
+    zp::clear_error();
+    if (!st || !hp || !sc) return fail(ZERO_ERR_INVALID_ARG, "zero_shard_step: NULL state, hparams or scaler");
+    const int64_t S = st->shard_elems;
+    if (S < 0) return fail(ZERO_ERR_INVALID_ARG, "shard_elems < 0");
+    if (S > std::numeric_limits<int64_t>::max() / 16) return fail(ZERO_ERR_INDEX_OVERFLOW, "shard too large");
+    if (R < 1 || R > zp::kMaxContrib) return fail(ZERO_ERR_INVALID_ARG, "R must be in 1..16");
+    if (st->cur != 0 && st->cur != 1) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 or 1");
+    if (st->t < 0 || st->t == std::numeric_limits<int64_t>::max())
+        return fail(ZERO_ERR_INVALID_ARG, "step count out of range");
+    const bool has1[3] = {st->p[1] != nullptr, st->m[1] != nullptr, st->v[1] != nullptr};
+    const bool pingpong = has1[0];
+    if (has1[1] != pingpong || has1[2] != pingpong)
+        return fail(ZERO_ERR_INVALID_ARG, "p[1], m[1], v[1] must be all set or all NULL");
+    if (!pingpong && st->cur != 0) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 in place");
+    if (!std::isfinite(sc->scale) || !(sc->scale > 0.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale must be finite and > 0");
+    if (!zp::finite_f(sc->backoff) || !(sc->backoff > 0.0f) || !zp::finite_f(sc->growth) ||
+        !(sc->growth > 0.0f) || !zp::finite_f(sc->min_scale) || sc->min_scale < 0.0f ||
+        sc->growth_interval < 0 || sc->good_steps < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "invalid loss-scaler settings");
+    if (!zp::finite_f(hp->lr) || !zp::finite_f(hp->eps) || !zp::finite_f(hp->weight_decay) ||
+        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "invalid Adam hyper-parameters (betas must be in [0, 1))");
+
+    if (S > 0) {
+        if (!grads) return fail(ZERO_ERR_INVALID_ARG, "grads is NULL");
+        for (int r = 0; r < R; ++r) {
+            if (!grads[r]) return fail(ZERO_ERR_INVALID_ARG, "a gradient pointer is NULL");
+            if (!zp::aligned(grads[r], 16)) return fail(ZERO_ERR_ALIGNMENT, "gradient not 16-byte aligned");
+        }
+        const int sets = pingpong ? 2 : 1;
+        zp::Range rs[7];
+        int nr = 0;
+        for (int k = 0; k < sets; ++k) {
+            const float* arr[3] = {st->p[k], st->m[k], st->v[k]};
+            for (const float* a : arr) {
+                if (!a) return fail(ZERO_ERR_INVALID_ARG, "a state pointer is NULL");
+                if (!zp::aligned(a, 16)) return fail(ZERO_ERR_ALIGNMENT, "state array not 16-byte aligned");
+                const uintptr_t lo = reinterpret_cast<uintptr_t>(a);
+                rs[nr++] = {lo, lo + uintptr_t(S) * 4};
+            }
+        }
+        if (!out_slot) return fail(ZERO_ERR_INVALID_ARG, "out_slot is NULL");
+        if (!zp::aligned(out_slot, 2)) return fail(ZERO_ERR_ALIGNMENT, "out_slot not 2-byte aligned");
+        const uintptr_t olo = reinterpret_cast<uintptr_t>(out_slot);
+        rs[nr++] = {olo, olo + uintptr_t(S) * 2};
+        for (int i = 0; i < nr; ++i)
+            for (int j = i + 1; j < nr; ++j)
+                if (zp::overlap(rs[i], rs[j]))
+                    return fail(ZERO_ERR_INVALID_ARG, "state arrays and slot must not overlap");
+        for (int r = 0; r < R; ++r) {
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(grads[r]);
+            const zp::Range g = {lo, lo + uintptr_t(S) * 2};
+            for (int i = 0; i < nr; ++i)
+                if (zp::overlap(g, rs[i]))
+                    return fail(ZERO_ERR_INVALID_ARG, "a gradient overlaps a written array");
+        }
+    }
+
+    int32_t flag = 0;
+    if (S > 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+        zp::DeviceWorkspace* ws = nullptr;
+        int rc = zp::get_workspace(dev, &ws);
+        if (rc != ZERO_OK) return rc;
+        std::lock_guard<std::mutex> lock(ws->mu);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+
+        if (++ws->epoch == 0) {   // the flag word holds epochs; restart after wrap-around
+            e = hipMemsetAsync(ws->d_flag, 0, sizeof(uint32_t), s);
+            if (e != hipSuccess) return zp::fail_hip(e, "hipMemsetAsync (flag)");
+            ws->epoch = 1;
+        }
+
+        // Adam constants for step t + 1 (used only if the step is taken)
+        const int64_t t_new = st->t + 1;
+        zp::StepLaunch a;
+        std::memset(&a, 0, sizeof(a));
+        for (int r = 0; r < R; ++r) a.grad[r] = grads[r];
+        a.R = R;
+        const int cur = st->cur;
+        a.p_in = st->p[cur];
+        a.m_in = st->m[cur];
+        a.v_in = st->v[cur];
+        a.p_out = pingpong ? st->p[1 - cur] : st->p[0];
+        a.m_out = pingpong ? st->m[1 - cur] : st->m[0];
+        a.v_out = pingpong ? st->v[1 - cur] : st->v[0];
+        a.out16 = out_slot;
+        a.n = S;
+        a.inv_scale = 1.0f / sc->scale;
+        a.lr = hp->lr;
+        a.beta1 = hp->beta1;
+        a.beta2 = hp->beta2;
+        a.one_minus_beta1 = 1.0f - hp->beta1;
+        a.one_minus_beta2 = 1.0f - hp->beta2;
+        a.bias_corr1 = float(1.0 - std::pow(double(hp->beta1), double(t_new)));
+        a.bias_corr2 = float(1.0 - std::pow(double(hp->beta2), double(t_new)));
+        a.eps = hp->eps;
+        a.weight_decay = hp->weight_decay;
+        a.flag = ws->d_flag;
+        a.epoch = ws->epoch;
+
+        if (pingpong) {
+            e = zp::launch_fused_step(a, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "shard step kernel launch");
+        } else {
+            e = zp::launch_check(a, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "check kernel launch");
+            e = zp::launch_update_in_place(a, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "update kernel launch");
+        }
+        e = hipMemcpyAsync(ws->h_flag, ws->d_flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "reading the overflow flag");
+        flag = (*ws->h_flag == ws->epoch) ? 1 : 0;
+
+        if (flag && pingpong) {
+            // the pass wrote the slot speculatively; restore fp16(master)
+            zp::StepLaunch r = a;
+            r.p_in = st->p[cur];
+            e = zp::launch_slot_from_master(r, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "slot restore kernel launch");
+        }
+    }
+
+    // commit or skip, and the loss scale
+    if (flag) {
+        float ns = sc->scale * sc->backoff;
+        if (ns < sc->min_scale) ns = sc->min_scale;
+        sc->scale = ns;
+        sc->good_steps = 0;
+    } else {
+        st->t += 1;
+        if (pingpong) st->cur = 1 - st->cur;
+        sc->good_steps += 1;
+        if (sc->growth_interval > 0 && sc->good_steps >= sc->growth_interval) {
+            const float ns = sc->scale * sc->growth;
+            if (std::isfinite(ns)) sc->scale = ns;   // never grow into inf
+            sc->good_steps = 0;
+        }
+    }
+    if (overflow) *overflow = flag;
+    return ZERO_OK;
+}
+
+extern "C" int zero_version(void) { return ZERO_PARTITION_VERSION; }
+
+extern "C" const char* zero_last_error(void) { return zp::g_last_error.c_str(); }
+
+extern "C" int zero_last_hip_error(void) { return zp::g_last_hip_error; }
+
+extern "C" int64_t zero_abi_struct_size(int32_t which) {
+    switch (which) {
+        case 0: return int64_t(sizeof(zero_layout_info));
+        case 1: return int64_t(sizeof(zero_segment));
+        case 2: return int64_t(sizeof(zero_shard_state));
+        case 3: return int64_t(sizeof(zero_adam_hparams));
+        case 4: return int64_t(sizeof(zero_loss_scaler));
+        default: return -1;
+    }
+}
+
+extern "C" int zero_device_info(int32_t* arch, int64_t* hbm_bytes) {
+    zp::clear_error();
+    if (!arch || !hbm_bytes) return fail(ZERO_ERR_INVALID_ARG, "zero_device_info: NULL argument");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDeviceProperties");
+    int num = 0;
+    if (std::sscanf(prop.gcnArchName, "gfx%d", &num) != 1) num = 0;
+    *arch = num;
+    *hbm_bytes = int64_t(prop.totalGlobalMem);
+    return ZERO_OK;
+}

@@ -1,0 +1,394 @@
+// layout.cpp -- partition layout and bucket plan (host only).
+//
+// Follows the ZeRO explainer page ("ZeRO: Memory Optimizations Toward
+// Training Trillion Parameter Models", azimuth.plus):
+//   - model-states paragraph: 2 + 2 + 4 + 4 + 4 bytes of model state per
+//     parameter (fp16 parameter, fp16 gradient, fp32 master/momentum/variance);
+//   - Stage 1/2/3 paragraphs: optimizer state, then gradients, then fp16
+//     parameters are kept as 1/N slices per rank;
+//   - constant-size buffers paragraph: gradients stream through one buffer of
+//     fixed size B, filled window by window.
+// The flattened vector (tensors back to back in list order) is cut into N
+// equal shards of S = roundup(ceil(Psi / N), A) elements; the last shards
+// carry the padding.  Segments are the pieces of each tensor between
+// consecutive shard (and bucket) boundaries.
+#include <algorithm>
+#include <cstring>
+#include <limits>
+#include <mutex>
+#include <new>
+
+#include "zp_internal.hpp"
+
+struct zero_layout {
+    std::vector<int64_t> numel;
+    std::vector<int64_t> offset;
+    int32_t n_ranks = 1;
+    int32_t stage = 0;
+    int64_t align = 1;
+    int64_t bucket = 0;
+    int64_t psi = 0;
+    int64_t shard = 0;
+    int64_t n_fills = 0;
+    std::vector<zero_segment> seg;
+
+    // device tables of the pack (filled by zero_layout_bind_tensors)
+    int device = -1;
+    zp::PackSrc* d_src = nullptr;
+    int32_t* d_first = nullptr;
+    int32_t n_src = 0;
+    int32_t chunk_shift = 0;
+    int cu_count = 0;
+};
+
+namespace {
+
+constexpr int64_t kMaxSegments = int64_t(1) << 26;
+constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
+
+bool add_overflows(int64_t a, int64_t b) { return a > kI64Max - b; }
+
+void free_device_tables(zero_layout* l) {
+    if (l->d_src) (void)hipFree(l->d_src);
+    if (l->d_first) (void)hipFree(l->d_first);
+    l->d_src = nullptr;
+    l->d_first = nullptr;
+    l->device = -1;
+    l->n_src = 0;
+}
+
+// End of the segment starting at flat index cur inside a tensor ending at
+// end: the next shard boundary, the next bucket boundary (bucket > 0) or the
+// tensor end, whichever comes first.  Written so that no sum can overflow.
+int64_t next_cut(int64_t cur, int64_t end, int64_t shard, int64_t bucket) {
+    int64_t cut = end;
+    const int64_t to_shard = shard - cur % shard;
+    if (to_shard < cut - cur) cut = cur + to_shard;
+    if (bucket > 0) {
+        const int64_t to_bucket = bucket - cur % bucket;
+        if (to_bucket < cut - cur) cut = cur + to_bucket;
+    }
+    return cut;
+}
+
+// Partitioned kinds per stage, in the order param16, grad16, master, m, v.
+bool partitioned(int stage, int kind) {
+    switch (stage) {
+        case 0: return false;
+        case 1: return kind >= 2;
+        case 2: return kind >= 1;
+        default: return true;
+    }
+}
+
+}  // namespace
+
+extern "C" int zero_partition_layout(const int64_t* numel, int64_t n_tensors, int32_t n_ranks,
+                                     int32_t stage, int64_t align_elems, int64_t bucket_elems,
+                                     zero_layout** out) {
+    zp::clear_error();
+    if (!out) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_partition_layout: out is NULL");
+    if (n_tensors < 0) return zp::fail(ZERO_ERR_INVALID_ARG, "n_tensors < 0");
+    if (n_tensors > 0 && !numel) return zp::fail(ZERO_ERR_INVALID_ARG, "numel is NULL");
+    if (n_tensors > std::numeric_limits<int32_t>::max())
+        return zp::fail(ZERO_ERR_INVALID_ARG, "more than 2^31-1 tensors");
+    if (n_ranks < 1) return zp::fail(ZERO_ERR_INVALID_ARG, "n_ranks < 1");
+    if (stage < 0 || stage > 3) return zp::fail(ZERO_ERR_INVALID_ARG, "stage must be 0..3");
+    if (align_elems < 1) return zp::fail(ZERO_ERR_INVALID_ARG, "align_elems < 1");
+    if (bucket_elems < 0) return zp::fail(ZERO_ERR_INVALID_ARG, "bucket_elems < 0");
+
+    int64_t psi = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        if (numel[i] < 0) return zp::fail(ZERO_ERR_INVALID_ARG, "negative tensor size");
+        if (add_overflows(psi, numel[i]))
+            return zp::fail(ZERO_ERR_INDEX_OVERFLOW, "sum of tensor sizes overflows int64");
+        psi += numel[i];
+    }
+    // S = roundup(ceil(psi / N), A), and 16 bytes for each of N * S elements
+    // must stay representable
+    const int64_t per = psi / n_ranks + (psi % n_ranks != 0);
+    const int64_t rem = per % align_elems;
+    if (rem != 0 && add_overflows(per, align_elems - rem))
+        return zp::fail(ZERO_ERR_INDEX_OVERFLOW, "shard size overflows int64");
+    const int64_t shard = rem ? per + (align_elems - rem) : per;
+    if (shard > 0 && shard > kI64Max / 16 / n_ranks)
+        return zp::fail(ZERO_ERR_INDEX_OVERFLOW, "16 * n_ranks * shard bytes overflow int64");
+
+    // count the segments before building them
+    int64_t n_seg = 0;
+    for (int64_t i = 0, off = 0; i < n_tensors; off += numel[i], ++i) {
+        int64_t cur = off, end = off + numel[i];
+        while (cur < end) {
+            cur = next_cut(cur, end, shard, bucket_elems);
+            if (++n_seg > kMaxSegments)
+                return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "layout would hold more than 2^26 segments");
+        }
+    }
+
+    zero_layout* l = new (std::nothrow) zero_layout();
+    if (!l) return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "layout allocation failed");
+    try {
+        l->numel.assign(numel, numel + n_tensors);
+        l->offset.resize(size_t(n_tensors));
+        l->seg.reserve(size_t(n_seg));
+    } catch (...) {
+        delete l;
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "layout allocation failed");
+    }
+    l->n_ranks = n_ranks;
+    l->stage = stage;
+    l->align = align_elems;
+    l->bucket = bucket_elems;
+    l->psi = psi;
+    l->shard = shard;
+    l->n_fills = bucket_elems > 0 ? psi / bucket_elems + (psi % bucket_elems != 0) : 0;
+
+    int64_t off = 0;
+    for (int64_t i = 0; i < n_tensors; ++i) {
+        l->offset[size_t(i)] = off;
+        const int64_t end = off + numel[i];
+        for (int64_t cur = off; cur < end;) {
+            zero_segment s;
+            s.tensor = int32_t(i);
+            s.owner = int32_t(cur / shard);
+            const int64_t cut = next_cut(cur, end, shard, bucket_elems);
+            if (bucket_elems > 0) {
+                s.fill = cur / bucket_elems;
+                s.bucket_off = cur - s.fill * bucket_elems;
+            } else {
+                s.fill = -1;
+                s.bucket_off = -1;
+            }
+            s.tensor_off = cur - off;
+            s.flat_off = cur;
+            s.len = cut - cur;
+            s.shard_off = cur - int64_t(s.owner) * shard;
+            l->seg.push_back(s);
+            cur = cut;
+        }
+        off = end;
+    }
+    *out = l;
+    return ZERO_OK;
+}
+
+extern "C" int zero_layout_destroy(zero_layout* layout) {
+    zp::clear_error();
+    if (!layout) return ZERO_OK;
+    free_device_tables(layout);
+    delete layout;
+    return ZERO_OK;
+}
+
+extern "C" int zero_layout_get_info(const zero_layout* l, zero_layout_info* info) {
+    zp::clear_error();
+    if (!l || !info) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_layout_get_info: NULL argument");
+    zero_layout_info r;
+    std::memset(&r, 0, sizeof(r));
+    r.psi = l->psi;
+    r.shard_elems = l->shard;
+    r.padded_elems = int64_t(l->n_ranks) * l->shard;
+    r.padding = r.padded_elems - l->psi;
+    r.n_tensors = int64_t(l->numel.size());
+    r.align_elems = l->align;
+    r.bucket_elems = l->bucket;
+    r.n_fills = l->n_fills;
+    r.n_segments = int64_t(l->seg.size());
+    r.n_ranks = l->n_ranks;
+    r.stage = l->stage;
+    static const int64_t kBytes[5] = {2, 2, 4, 4, 4};
+    int64_t* dst[5] = {&r.bytes_param16, &r.bytes_grad16, &r.bytes_master, &r.bytes_momentum,
+                       &r.bytes_variance};
+    for (int k = 0; k < 5; ++k) {
+        *dst[k] = kBytes[k] * (partitioned(l->stage, k) ? l->shard : l->psi);
+        r.bytes_total += *dst[k];
+    }
+    *info = r;
+    return ZERO_OK;
+}
+
+extern "C" int zero_layout_tensor_offsets(const zero_layout* l, int64_t* out, int64_t cap) {
+    zp::clear_error();
+    if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    const int64_t n = int64_t(l->offset.size());
+    if (cap < n || (n > 0 && !out))
+        return zp::fail(ZERO_ERR_CAPACITY, "tensor offset array too small");
+    if (n > 0) std::memcpy(out, l->offset.data(), size_t(n) * sizeof(int64_t));
+    return ZERO_OK;
+}
+
+extern "C" int zero_layout_rank_range(const zero_layout* l, int32_t rank, int64_t* begin,
+                                      int64_t* real_end, int64_t* end) {
+    zp::clear_error();
+    if (!l || !begin || !real_end || !end)
+        return zp::fail(ZERO_ERR_INVALID_ARG, "zero_layout_rank_range: NULL argument");
+    if (rank < 0 || rank >= l->n_ranks) return zp::fail(ZERO_ERR_INVALID_ARG, "rank out of range");
+    const int64_t b = int64_t(rank) * l->shard;
+    const int64_t e = b + l->shard;
+    *begin = b;
+    *end = e;
+    *real_end = std::max(b, std::min(e, l->psi));
+    return ZERO_OK;
+}
+
+namespace {
+
+int copy_range(const zero_layout* l, size_t lo, size_t hi, zero_segment* out, int64_t cap,
+               int64_t* n_out) {
+    const int64_t n = int64_t(hi - lo);
+    *n_out = n;
+    if (cap < n || (n > 0 && !out)) return zp::fail(ZERO_ERR_CAPACITY, "segment array too small");
+    if (n > 0) std::memcpy(out, l->seg.data() + lo, size_t(n) * sizeof(zero_segment));
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" int zero_layout_segments(const zero_layout* l, zero_segment* out, int64_t cap,
+                                    int64_t* n_out) {
+    zp::clear_error();
+    if (!l || !n_out) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_layout_segments: NULL argument");
+    return copy_range(l, 0, l->seg.size(), out, cap, n_out);
+}
+
+extern "C" int zero_layout_rank_segments(const zero_layout* l, int32_t rank, zero_segment* out,
+                                         int64_t cap, int64_t* n_out) {
+    zp::clear_error();
+    if (!l || !n_out) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_layout_rank_segments: NULL argument");
+    if (rank < 0 || rank >= l->n_ranks) return zp::fail(ZERO_ERR_INVALID_ARG, "rank out of range");
+    // segments are sorted by flat offset, so owners never decrease
+    auto lo = std::lower_bound(l->seg.begin(), l->seg.end(), rank,
+                               [](const zero_segment& s, int32_t r) { return s.owner < r; });
+    auto hi = std::lower_bound(lo, l->seg.end(), rank + 1,
+                               [](const zero_segment& s, int32_t r) { return s.owner < r; });
+    return copy_range(l, size_t(lo - l->seg.begin()), size_t(hi - l->seg.begin()), out, cap, n_out);
+}
+
+extern "C" int zero_layout_fill_segments(const zero_layout* l, int64_t fill, zero_segment* out,
+                                         int64_t cap, int64_t* n_out) {
+    zp::clear_error();
+    if (!l || !n_out) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_layout_fill_segments: NULL argument");
+    if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (fill < 0 || fill >= l->n_fills) return zp::fail(ZERO_ERR_INVALID_ARG, "fill out of range");
+    auto lo = std::lower_bound(l->seg.begin(), l->seg.end(), fill,
+                               [](const zero_segment& s, int64_t f) { return s.fill < f; });
+    auto hi = std::lower_bound(lo, l->seg.end(), fill + 1,
+                               [](const zero_segment& s, int64_t f) { return s.fill < f; });
+    return copy_range(l, size_t(lo - l->seg.begin()), size_t(hi - l->seg.begin()), out, cap, n_out);
+}
+
+// ---------------------------------------------------------------------------
+// bucket pack: device tables and launch
+// ---------------------------------------------------------------------------
+
+extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* dev_ptrs,
+                                        void* stream) {
+    zp::clear_error();
+    if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    const size_t nt = l->numel.size();
+    if (nt > 0 && !dev_ptrs) return zp::fail(ZERO_ERR_INVALID_ARG, "dev_ptrs is NULL");
+
+    std::vector<zp::PackSrc> src;
+    try {
+        src.reserve(nt);
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
+    for (size_t i = 0; i < nt; ++i) {
+        if (l->numel[i] == 0) continue;
+        if (!dev_ptrs[i]) return zp::fail(ZERO_ERR_INVALID_ARG, "NULL pointer for a non-empty tensor");
+        if (reinterpret_cast<uintptr_t>(dev_ptrs[i]) & 1)
+            return zp::fail(ZERO_ERR_ALIGNMENT, "tensor pointer not 2-byte aligned");
+        src.push_back({dev_ptrs[i], l->offset[i], l->numel[i]});
+    }
+    if (src.size() > size_t(std::numeric_limits<int32_t>::max()))
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
+
+    // chunk index: first[c] = source holding flat index c << shift.  The chunk
+    // is at least 4096 elements and grows so that the table stays <= 2^22.
+    int shift = 12;
+    while (((l->psi + (int64_t(1) << shift) - 1) >> shift) > (int64_t(1) << 22)) ++shift;
+    const int64_t n_chunks = (l->psi + (int64_t(1) << shift) - 1) >> shift;
+    std::vector<int32_t> first;
+    try {
+        first.resize(size_t(n_chunks) + 1);
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
+    size_t s = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const int64_t g = c << shift;
+        while (s + 1 < src.size() && src[s + 1].flat_off <= g) ++s;
+        first[size_t(c)] = int32_t(s);
+    }
+    first[size_t(n_chunks)] = src.empty() ? 0 : int32_t(src.size() - 1);
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipDeviceGetAttribute");
+
+    zp::PackSrc* d_src = nullptr;
+    int32_t* d_first = nullptr;
+    const size_t src_bytes = std::max<size_t>(1, src.size()) * sizeof(zp::PackSrc);
+    const size_t first_bytes = first.size() * sizeof(int32_t);
+    e = hipMalloc(reinterpret_cast<void**>(&d_src), src_bytes);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipMalloc (pack sources)");
+    e = hipMalloc(reinterpret_cast<void**>(&d_first), first_bytes);
+    if (e != hipSuccess) {
+        (void)hipFree(d_src);
+        return zp::fail_hip(e, "hipMalloc (pack chunk index)");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!src.empty()) e = hipMemcpyAsync(d_src, src.data(), src.size() * sizeof(zp::PackSrc),
+                                         hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(d_first, first.data(), first_bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        (void)hipFree(d_src);
+        (void)hipFree(d_first);
+        return zp::fail_hip(e, "uploading pack tables");
+    }
+    free_device_tables(l);
+    l->d_src = d_src;
+    l->d_first = d_first;
+    l->n_src = int32_t(src.size());
+    l->chunk_shift = shift;
+    l->device = dev;
+    l->cu_count = cus;
+    return ZERO_OK;
+}
+
+extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bucket, void* stream,
+                                int64_t* packed_elems) {
+    zp::clear_error();
+    if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (l->device < 0) return zp::fail(ZERO_ERR_STATE, "tensors not bound (zero_layout_bind_tensors)");
+    if (fill < 0 || fill >= l->n_fills) return zp::fail(ZERO_ERR_INVALID_ARG, "fill out of range");
+    if (!bucket) return zp::fail(ZERO_ERR_INVALID_ARG, "bucket is NULL");
+    if (reinterpret_cast<uintptr_t>(bucket) & 15)
+        return zp::fail(ZERO_ERR_ALIGNMENT, "bucket not 16-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    if (dev != l->device) return zp::fail(ZERO_ERR_STATE, "layout was bound on another device");
+
+    zp::PackLaunch a;
+    a.src = l->d_src;
+    a.first = l->d_first;
+    a.n_src = l->n_src;
+    a.chunk_shift = l->chunk_shift;
+    a.psi = l->psi;
+    a.fill_base = fill * l->bucket;
+    a.bucket_elems = l->bucket;
+    a.bucket = bucket;
+    e = zp::launch_pack(a, l->cu_count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return zp::fail_hip(e, "pack kernel launch");
+    if (packed_elems) *packed_elems = std::min(l->bucket, l->psi - a.fill_base);
+    return ZERO_OK;
+}

@@ -1,0 +1,317 @@
+// shard_step.hip -- fused ZeRO-DP shard step for gfx950.
+//
+// One rank's share of the optimizer step, per the ZeRO explainer page
+// ("ZeRO: Memory Optimizations Toward Training Trillion Parameter Models",
+// azimuth.plus):
+//   - Stage 2 (P_os+g) paragraph: the rank ends up with only its slice of the
+//     reduced gradients; locally that is the sum of R fp16 contributions;
+//   - Stage 1 (P_os) paragraph: the rank updates only its partition of the
+//     parameters with its partition of the fp32 Adam state (model-states
+//     paragraph: master copy, momentum, variance), and the new fp16
+//     parameters go to its slot of the gather buffer for the all-gather.
+// Adam is the textbook bias-corrected form (the page names Adam but does not
+// write it out); a step with any inf/NaN in the reduced gradients is skipped
+// (dynamic loss scaling; not on the page).
+//
+// Every element is independent and the kernel moves 26 + 2R bytes per element
+// for about 60 ALU operations, so it is bound by HBM bandwidth.  Design:
+//   - grid-stride loop over 8-element vectors: one 128-bit load per fp16
+//     contribution (8 halves), two 128-bit loads per fp32 array, the same
+//     stores; a scalar tail for S mod 8;
+//   - the fp32 arithmetic is written in the order of the definition with one
+//     rounding per operation (no contraction, IEEE division and square root),
+//     so the results match a scalar reference bit for bit;
+//   - the overflow flag is a wave-level ballot followed by one atomic per
+//     wave that saw a non-finite sum; the flag word holds the epoch of the
+//     call that raised it, so it never has to be cleared between calls;
+//   - ping-pong state (read set A, write set B) makes the step a single pass:
+//     the commit is the host flipping the live set once the flag is known.
+#include "zp_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace zp {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+
+// fp16 slot alignment classes
+constexpr int kOut16B = 0;
+constexpr int kOut8B = 1;
+constexpr int kOut4B = 2;
+constexpr int kOut2B = 3;
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(x)));
+}
+
+__device__ __forceinline__ bool not_finite(float x) {
+    return (__builtin_bit_cast(uint32_t, x) & 0x7F800000u) == 0x7F800000u;
+}
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
+
+// Textbook Adam on one element, one rounding per operation.
+__device__ __forceinline__ void adam_element(const StepLaunch& a, float sum, float& p, float& m,
+                                             float& v) {
+    float g = sum * a.inv_scale;
+    if (a.weight_decay != 0.0f) g = g + a.weight_decay * p;
+    const float mi = a.beta1 * m + a.one_minus_beta1 * g;
+    const float vi = a.beta2 * v + a.one_minus_beta2 * (g * g);
+    const float mhat = mi / a.bias_corr1;
+    const float vhat = vi / a.bias_corr2;
+    const float den = __builtin_sqrtf(vhat) + a.eps;
+    p = p - a.lr * (mhat / den);
+    m = mi;
+    v = vi;
+}
+
+// Sum of the R contributions for 8 consecutive elements starting at e0.
+// R == 0 selects the run-time count a.R (1..16).
+template <int R>
+__device__ __forceinline__ void reduce8(const StepLaunch& a, int64_t e0, float s[8]) {
+    const u32x4 c0 = load_stream(reinterpret_cast<const u32x4*>(a.grad[0] + e0));
+    const uint32_t w0[4] = {c0.x, c0.y, c0.z, c0.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s[k] = h2f(w0[k >> 1] >> (16 * (k & 1)));
+    constexpr int kMax = R == 0 ? kMaxContrib : R;
+#pragma unroll
+    for (int r = 1; r < kMax; ++r) {
+        if (R == 0 && r >= a.R) break;
+        const u32x4 c = load_stream(reinterpret_cast<const u32x4*>(a.grad[r] + e0));
+        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] = s[k] + h2f(w[k >> 1] >> (16 * (k & 1)));
+    }
+}
+
+template <int R>
+__device__ __forceinline__ float reduce1(const StepLaunch& a, int64_t e) {
+    float s = h2f(a.grad[0][e]);
+    constexpr int kMax = R == 0 ? kMaxContrib : R;
+#pragma unroll
+    for (int r = 1; r < kMax; ++r) {
+        if (R == 0 && r >= a.R) break;
+        s = s + h2f(a.grad[r][e]);
+    }
+    return s;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_half8(uint16_t* dst, const float p[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] = f2h(p[2 * d]) | (f2h(p[2 * d + 1]) << 16);
+    if (OUT == kOut16B) {
+        store_stream(reinterpret_cast<u32x4*>(dst), u32x4{w[0], w[1], w[2], w[3]});
+    } else if (OUT == kOut8B) {
+        store_stream(reinterpret_cast<u32x2*>(dst), u32x2{w[0], w[1]});
+        store_stream(reinterpret_cast<u32x2*>(dst + 4), u32x2{w[2], w[3]});
+    } else if (OUT == kOut4B) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) store_stream(reinterpret_cast<uint32_t*>(dst + 2 * d), w[d]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[k] = uint16_t(w[k >> 1] >> (16 * (k & 1)));
+    }
+}
+
+__device__ __forceinline__ void raise_flag(const StepLaunch& a, bool bad) {
+    // every lane of every wave reaches this point
+    const unsigned long long ballot = __ballot(bad);
+    if (ballot != 0ull && (threadIdx.x & 63) == 0) atomicMax(a.flag, a.epoch);
+}
+
+// The fused step.  kFlag: compute and raise the overflow flag.  kSkip: in
+// place, after the check pass -- do nothing if the flag holds this epoch.
+template <int R, int OUT, bool kFlag, bool kSkip>
+__global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
+    if (kSkip && __atomic_load_n(a.flag, __ATOMIC_RELAXED) == a.epoch) return;
+    const int64_t nvec = a.n >> 3;
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    bool bad = false;
+    for (int64_t i = tid; i < nvec; i += stride) {
+        const int64_t e0 = i << 3;
+        float s[8];
+        reduce8<R>(a, e0, s);
+        const f32x4 p0 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0));
+        const f32x4 p1 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0 + 4));
+        const f32x4 m0 = load_stream(reinterpret_cast<const f32x4*>(a.m_in + e0));
+        const f32x4 m1 = load_stream(reinterpret_cast<const f32x4*>(a.m_in + e0 + 4));
+        const f32x4 v0 = load_stream(reinterpret_cast<const f32x4*>(a.v_in + e0));
+        const f32x4 v1 = load_stream(reinterpret_cast<const f32x4*>(a.v_in + e0 + 4));
+        float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (kFlag) bad |= not_finite(s[k]);
+            adam_element(a, s[k], p[k], m[k], v[k]);
+        }
+        store_stream(reinterpret_cast<f32x4*>(a.p_out + e0), f32x4{p[0], p[1], p[2], p[3]});
+        store_stream(reinterpret_cast<f32x4*>(a.p_out + e0 + 4), f32x4{p[4], p[5], p[6], p[7]});
+        store_stream(reinterpret_cast<f32x4*>(a.m_out + e0), f32x4{m[0], m[1], m[2], m[3]});
+        store_stream(reinterpret_cast<f32x4*>(a.m_out + e0 + 4), f32x4{m[4], m[5], m[6], m[7]});
+        store_stream(reinterpret_cast<f32x4*>(a.v_out + e0), f32x4{v[0], v[1], v[2], v[3]});
+        store_stream(reinterpret_cast<f32x4*>(a.v_out + e0 + 4), f32x4{v[4], v[5], v[6], v[7]});
+        store_half8<OUT>(a.out16 + e0, p);
+    }
+    // the last S mod 8 elements, one per thread
+    const int64_t tail = a.n - (nvec << 3);
+    if (tid < tail) {
+        const int64_t e = (nvec << 3) + tid;
+        const float s = reduce1<R>(a, e);
+        if (kFlag) bad |= not_finite(s);
+        float p = a.p_in[e], m = a.m_in[e], v = a.v_in[e];
+        adam_element(a, s, p, m, v);
+        a.p_out[e] = p;
+        a.m_out[e] = m;
+        a.v_out[e] = v;
+        a.out16[e] = uint16_t(f2h(p));
+    }
+    if (kFlag) raise_flag(a, bad);
+}
+
+// In-place pass 1: overflow check over the contributions alone.  A sum of at
+// most 16 finite fp16 values is finite in fp32 (16 * 65504 << FLT_MAX), and
+// inf or NaN in any input makes the fp32 sum inf or NaN, so "some sum is not
+// finite" is "some input has the all-ones fp16 exponent".
+__device__ __forceinline__ bool half_special(uint32_t w) {
+    return ((w & 0x7C00u) == 0x7C00u) || ((w & 0x7C000000u) == 0x7C000000u);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void check_kernel(const StepLaunch a) {
+    const int64_t nvec = a.n >> 3;
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    bool bad = false;
+    constexpr int kMax = R == 0 ? kMaxContrib : R;
+    for (int64_t i = tid; i < nvec; i += stride) {
+#pragma unroll
+        for (int r = 0; r < kMax; ++r) {
+            if (R == 0 && r >= a.R) break;
+            const u32x4 c = load_stream(reinterpret_cast<const u32x4*>(a.grad[r] + (i << 3)));
+            bad = bad || half_special(c.x) || half_special(c.y) || half_special(c.z) || half_special(c.w);
+        }
+    }
+    const int64_t tail = a.n - (nvec << 3);
+    if (tid < tail) {
+        const int64_t e = (nvec << 3) + tid;
+#pragma unroll
+        for (int r = 0; r < kMax; ++r) {
+            if (R == 0 && r >= a.R) break;
+            bad |= (a.grad[r][e] & 0x7C00u) == 0x7C00u;
+        }
+    }
+    raise_flag(a, bad);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void slot_kernel(const StepLaunch a) {
+    const int64_t nvec = a.n >> 3;
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    for (int64_t i = tid; i < nvec; i += stride) {
+        const int64_t e0 = i << 3;
+        const f32x4 p0 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0));
+        const f32x4 p1 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0 + 4));
+        const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        store_half8<OUT>(a.out16 + e0, p);
+    }
+    const int64_t tail = a.n - (nvec << 3);
+    if (tid < tail) {
+        const int64_t e = (nvec << 3) + tid;
+        a.out16[e] = uint16_t(f2h(a.p_in[e]));
+    }
+}
+
+int out_class(const uint16_t* p) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(p);
+    if ((x & 15) == 0) return kOut16B;
+    if ((x & 7) == 0) return kOut8B;
+    if ((x & 3) == 0) return kOut4B;
+    return kOut2B;
+}
+
+dim3 grid_for(int64_t n, int cu_count, int per_cu) {
+    const int64_t nvec = n >> 3;
+    int64_t blocks = (nvec + kThreads - 1) / kThreads;
+    const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * per_cu;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;   // the tail needs one block even when nvec == 0
+    return dim3(unsigned(blocks));
+}
+
+template <bool kFlag, bool kSkip, int R>
+void launch_step_r(const StepLaunch& a, dim3 grid, hipStream_t s) {
+    switch (out_class(a.out16)) {
+        case kOut16B: hipLaunchKernelGGL((step_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut8B: hipLaunchKernelGGL((step_kernel<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut4B: hipLaunchKernelGGL((step_kernel<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_kernel<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+    }
+}
+
+template <bool kFlag, bool kSkip>
+void launch_step(const StepLaunch& a, dim3 grid, hipStream_t s) {
+    switch (a.R) {
+        case 1: launch_step_r<kFlag, kSkip, 1>(a, grid, s); break;
+        case 2: launch_step_r<kFlag, kSkip, 2>(a, grid, s); break;
+        case 4: launch_step_r<kFlag, kSkip, 4>(a, grid, s); break;
+        default: launch_step_r<kFlag, kSkip, 0>(a, grid, s); break;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream) {
+    launch_step<true, false>(a, grid_for(a.n, cu_count, blocks_per_cu_step()), stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t stream) {
+    launch_step<false, true>(a, grid_for(a.n, cu_count, blocks_per_cu_step()), stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream) {
+    const dim3 grid = grid_for(a.n, cu_count, blocks_per_cu_step());
+    switch (a.R) {
+        case 1: hipLaunchKernelGGL(check_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(check_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(check_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(check_kernel<0>, grid, dim3(kThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_slot_from_master(const StepLaunch& a, int cu_count, hipStream_t stream) {
+    const dim3 grid = grid_for(a.n, cu_count, blocks_per_cu_step());
+    switch (out_class(a.out16)) {
+        case kOut16B: hipLaunchKernelGGL(slot_kernel<kOut16B>, grid, dim3(kThreads), 0, stream, a); break;
+        case kOut8B: hipLaunchKernelGGL(slot_kernel<kOut8B>, grid, dim3(kThreads), 0, stream, a); break;
+        case kOut4B: hipLaunchKernelGGL(slot_kernel<kOut4B>, grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(slot_kernel<kOut2B>, grid, dim3(kThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace zp

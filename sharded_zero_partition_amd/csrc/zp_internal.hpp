@@ -1,0 +1,98 @@
+// zp_internal.hpp -- declarations shared by the library's host and device
+// translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "zero_partition.h"
+
+namespace zp {
+
+// ---------------------------------------------------------------------------
+// error reporting (thread-local message, see capi.cpp)
+// ---------------------------------------------------------------------------
+int fail(int status, const std::string& msg);
+int fail_hip(hipError_t err, const char* what);
+void clear_error();
+
+// ---------------------------------------------------------------------------
+// pack kernel tables
+// ---------------------------------------------------------------------------
+
+// One non-empty tensor of the flattened stream, as the pack kernel sees it.
+struct PackSrc {
+    const uint16_t* ptr;  // device address of element 0
+    int64_t flat_off;     // first flat index
+    int64_t len;          // elements (> 0)
+};
+
+struct PackLaunch {
+    const PackSrc* src;       // device, n_src entries sorted by flat_off
+    const int32_t* first;     // device, n_chunks + 1 entries: src index holding
+                              // flat index c << chunk_shift (last entry n_src - 1)
+    int32_t n_src;
+    int32_t chunk_shift;
+    int64_t psi;
+    int64_t fill_base;        // fill * B
+    int64_t bucket_elems;     // B
+    uint16_t* bucket;         // device, 16-byte aligned
+};
+
+hipError_t launch_pack(const PackLaunch& a, int cu_count, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// shard step kernels
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxContrib = 16;
+
+struct StepLaunch {
+    const uint16_t* grad[kMaxContrib];  // R device pointers, 16-byte aligned
+    int32_t R;
+    const float* p_in;
+    const float* m_in;
+    const float* v_in;
+    float* p_out;       // == p_in in place
+    float* m_out;
+    float* v_out;
+    uint16_t* out16;    // fp16 slot, 2-byte aligned
+    int64_t n;          // S
+    float inv_scale;    // 1 / scale
+    float lr;
+    float beta1;
+    float beta2;
+    float one_minus_beta1;
+    float one_minus_beta2;
+    float bias_corr1;   // 1 - beta1^t
+    float bias_corr2;   // 1 - beta2^t
+    float eps;
+    float weight_decay;
+    uint32_t* flag;     // device word; set to `epoch` when a value is not finite
+    uint32_t epoch;
+};
+
+// One pass: reduce + finite check + Adam + fp16 cast, reading set *_in and
+// writing set *_out (distinct buffers); raises the flag.
+hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream);
+
+// In-place mode, pass 1: finite check over the R contributions only.
+hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream);
+
+// In-place mode, pass 2: the update, skipped by every thread when the flag
+// already holds `epoch`.
+hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t stream);
+
+// Rewrite the fp16 slot from the fp32 master values (restores the slot after
+// a skipped ping-pong step): out16[i] = fp16(p_in[i]).
+hipError_t launch_slot_from_master(const StepLaunch& a, int cu_count, hipStream_t stream);
+
+// Launch shape knobs (blocks per CU of the grid-stride kernels), read once
+// from ZERO_BLOCKS_PER_CU / ZERO_PACK_BLOCKS_PER_CU when set.
+int blocks_per_cu_step();
+int blocks_per_cu_pack();
+
+}  // namespace zp

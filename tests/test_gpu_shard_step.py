@@ -1,0 +1,152 @@
+"""GPU parity of the fused shard step (through the C ABI) against the CPU
+oracle: ragged sizes spanning several tiles, every contribution count path,
+both state modes, every slot alignment class, the overflow/skip path, fp16
+subnormals, padding, weight decay and the empty shard."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import SENTINEL, Lockstep, host_contribs
+
+pytestmark = pytest.mark.gpu
+
+HP = oracle.AdamHP(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def _p0(rng, S):
+    return torch.from_numpy(rng.standard_normal(S, dtype=np.float32) * np.float32(0.02))
+
+
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("S", [1, 7, 8, 9, 4093, 3 * 65536 + 5])
+def test_small_shards(S, R, pingpong):
+    rng = np.random.default_rng(1000 * S + 10 * R + int(pingpong))
+    ls = Lockstep(_p0(rng, S), R, HP, 1024.0, pingpong, slot_offset=8, slot_tail=9)
+    for _ in range(3):
+        ls.step(host_contribs(rng, S, R, 1024.0))
+    ls.check_sentinels()
+    assert ls.ts == [1, 2, 3]
+    assert ls.bit_exact
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 3, 4, 6])
+def test_slot_alignment_classes(offset):
+    """The slot may start at any element of the gather buffer (odd S makes
+    odd rank offsets): 16-, 8-, 4- and 2-byte aligned store paths."""
+    rng = np.random.default_rng(77 + offset)
+    S = 70001
+    ls = Lockstep(_p0(rng, S), 2, HP, 1024.0, True, slot_offset=offset, slot_tail=5)
+    for _ in range(2):
+        ls.step(host_contribs(rng, S, 2, 1024.0))
+    ls.check_sentinels()
+    assert ls.bit_exact
+
+
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+@pytest.mark.parametrize("where", ["first", "last", "tail", "middle"])
+@pytest.mark.parametrize("value", [0x7C00, 0xFC00, 0x7E00])
+def test_overflow_skips_step(pingpong, where, value):
+    rng = np.random.default_rng(5)
+    S, R = 50_003, 3
+    ls = Lockstep(_p0(rng, S), R, HP, 65536.0, pingpong, slot_offset=3)
+    ls.step(host_contribs(rng, S, R, 65536.0))
+    before = [x.clone() for x in ls.state.live()] + [ls.slot.clone()]
+    c = host_contribs(rng, S, R, 65536.0)
+    idx = {"first": 0, "last": S - 1, "tail": S - 2, "middle": S // 2}[where]
+    c[1][idx] = int(np.array(value, dtype=np.uint16).view(np.int16))
+    assert ls.step(c) == 1
+    after = list(ls.state.live()) + [ls.slot]
+    for a, b in zip(before, after):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+    assert ls.scaler.scale == 32768.0 and ls.state.t == 1
+    ls.step(host_contribs(rng, S, R, 32768.0))
+    assert ls.flags == [0, 1, 0] and ls.ts == [1, 1, 2]
+    ls.check_sentinels()
+    assert ls.bit_exact
+
+
+def test_fp16_subnormal_contributions():
+    rng = np.random.default_rng(9)
+    S, R = 65_539, 2
+    ls = Lockstep(_p0(rng, S), R, HP, 1.0, True)
+    for _ in range(3):
+        c = []
+        for _ in range(R):
+            bits = rng.integers(0, 0x0400, size=S, dtype=np.uint16)   # subnormals and zeros
+            bits |= (rng.integers(0, 2, size=S, dtype=np.uint16) << 15)
+            c.append(torch.from_numpy(bits.view(np.int16)).to("cuda"))
+        ls.step(c)
+    assert ls.bit_exact
+
+
+def test_padding_stays_zero():
+    rng = np.random.default_rng(10)
+    S, real = 4096 + 13, 4000
+    p0 = _p0(rng, S)
+    p0[real:] = 0
+    ls = Lockstep(p0, 2, HP, 1024.0, True)
+    for _ in range(3):
+        c = host_contribs(rng, S, 2, 1024.0)
+        for x in c:
+            x[real:] = 0
+        ls.step(c)
+    p, m, v = ls.state.live()
+    assert not p[real:].any() and not m[real:].any() and not v[real:].any()
+    assert not ls.slot[real:].any()
+    assert ls.bit_exact
+
+
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+def test_weight_decay(pingpong):
+    rng = np.random.default_rng(11)
+    S = 30_001
+    hp = oracle.AdamHP(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    ls = Lockstep(_p0(rng, S), 2, hp, 1024.0, pingpong)
+    for _ in range(4):
+        ls.step(host_contribs(rng, S, 2, 1024.0))
+    assert ls.bit_exact
+
+
+def test_many_contributions_and_repeated_inputs():
+    """R = 16 (the largest count) and aliased contribution buffers."""
+    rng = np.random.default_rng(12)
+    S = 9_999
+    ls = Lockstep(_p0(rng, S), 16, HP, 1024.0, False)
+    base = host_contribs(rng, S, 4, 1024.0)
+    ls.step([base[i % 4] for i in range(16)])
+    assert ls.bit_exact
+
+
+def test_empty_shard():
+    import sharded_zero_partition_amd as zp
+    e = torch.empty(0, dtype=torch.float32, device="cuda")
+    st = zp.ShardState(e, e.clone(), e.clone())
+    sc = zp.LossScaler.make(1024.0)
+    hpc = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    g = torch.empty(0, dtype=torch.int16, device="cuda")
+    assert zp.shard_step(st, [g, g], hpc, sc, g) == 0
+    assert st.t == 1 and sc.good_steps == 1
+
+
+def test_errors_leave_state_untouched():
+    import sharded_zero_partition_amd as zp
+    S = 1024
+    p = torch.zeros(S, device="cuda")
+    st = zp.ShardState(p, torch.zeros_like(p), torch.zeros_like(p))
+    sc = zp.LossScaler.make(1024.0)
+    hpc = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    g = torch.zeros(S + 8, dtype=torch.int16, device="cuda")
+    slot = torch.full((S,), SENTINEL, dtype=torch.int16, device="cuda")
+    with pytest.raises(zp.ZeroError, match="ALIGNMENT"):
+        zp.shard_step(st, [g[1:S + 1]], hpc, sc, slot)     # 2-byte aligned gradient
+    bad_hp = zp.AdamHParams(1e-4, 1.0, 0.999, 1e-8, 0.0)
+    with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+        zp.shard_step(st, [g[:S]], bad_hp, sc, slot)
+    with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+        zp.shard_step(st, [g[:S]], hpc, sc, p.view(torch.int16)[:S])   # slot overlaps p
+    assert st.t == 0 and sc.scale == 1024.0 and not p.any()
+    assert int((slot != SENTINEL).sum()) == 0
