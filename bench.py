@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's ZeRO-DP shard step on one MI355X.
+
+Workload (the 13B-parameter, N = 64 ZeRO-3 rank shard): a GPT-style model of
+40 layers, hidden 5120, FFN 20480, vocabulary 50257 (Psi = 12,848,143,360)
+cut into 64 shards; rank 63 owns S = 200,752,240 elements.  Per step it
+reduces R = 2 fp16 gradient contributions, unscales them with the overflow
+check, applies Adam to its fp32 master/momentum/variance shard and writes the
+fp16 parameters into its slot of a 64-slot gather buffer (25.7 GB).  All
+inputs are synthetic and resident in HBM before the timed region.
+
+A timed step is one zero_shard_step call (fused kernel, overflow read-back,
+loss-scale control).  The same run also reports
+  * the partition layout of the 484-tensor model (host, once per model),
+  * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
+  * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
+    HIP-event time on its stream) and, when the counter profile under
+    profiles/ was taken from the current kernel source, its measured traffic,
+  * the CPU oracle timed on the host on a bounded sample of the same shard.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("fused shard-step elements/s and achieved HBM GB/s (% of peak) per rank shard")
+HBM_PEAK_GBS = 8000.0
+PMC_PROFILE = os.path.join(ROOT, "profiles", "shard_step_zero3_13b_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "sharded_zero_partition_amd", "csrc", f)
+                  for f in ("shard_step.hip", "zp_internal.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(shard_elems: int):
+    """HBM bytes per launch from the committed counter profile, or None when
+    there is none or it was taken from another version of the kernel."""
+    if not os.path.exists(PMC_PROFILE):
+        return None
+    with open(PMC_PROFILE) as f:
+        prof = json.load(f)
+    if prof.get("kernel_source_sha") != kernel_source_hash() or prof.get("shard_elems") != shard_elems:
+        return None
+    return int(round((prof["fetch_kib_per_dispatch"] * prof["fetch_scale"] +
+                      prof["write_kib_per_dispatch"] * prof["write_scale"]) * 1024))
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["pingpong", "inplace"], default="pingpong")
+    ap.add_argument("--no-pack", action="store_true", help="skip the bucket-pack measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 2 GiB device copy (scale reference for HBM counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one rank's shard step on a single GPU; runs on more than "
+              "one GPU are not part of this build (the multi-GPU exchange is described in the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import numpy as np
+    import torch
+
+    import sharded_zero_partition_amd as zp
+    from sharded_zero_partition_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    w = W.zero3_13b()
+    S, R = w.shard, w.n_contrib
+
+    # a1: the partition layout of the model (host; once per model)
+    t0 = time.perf_counter()
+    lay = zp.partition_layout(w.numels, w.n_ranks, stage=w.stage)
+    layout_ms = (time.perf_counter() - t0) * 1e3
+    assert lay.info.shard_elems == S
+    begin, _, _ = lay.rank_range(w.rank)
+    lay.close()
+
+    # inputs resident in HBM
+    gather = torch.empty(w.gather_slots * S, dtype=torch.int16, device=dev)
+    slot = gather[w.rank * S:(w.rank + 1) * S]
+    p0 = W.master_init(w, device=dev)
+    slot.copy_(p0.to(torch.float16).view(torch.int16))
+    if args.mode == "pingpong":
+        st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0),
+                           torch.empty_like(p0), torch.empty_like(p0), torch.empty_like(p0))
+    else:
+        st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0))
+    grads = [W.grad_contribution(w, 1, r, w.scale, device=dev) for r in range(R)]
+    hp = zp.AdamHParams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+    scaler = zp.LossScaler.make(w.scale)
+
+    # host copy of the sample the CPU oracle will take (before any update)
+    cpu_n = min(S, 1 << 27)
+    cpu_inputs = None
+    if not args.no_cpu_baseline:
+        cpu_inputs = (p0[:cpu_n].cpu().numpy().copy(),
+                      [g[:cpu_n].cpu().numpy().view(np.uint16).copy() for g in grads])
+
+    for _ in range(args.warmup):
+        zp.shard_step(st, grads, hp, scaler, slot)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    zp.set_kernel_timing(True)
+    kernel_ms = []
+    flags = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        flags += zp.shard_step(st, grads, hp, scaler, slot)
+        kernel_ms.append(zp.last_kernel_ms())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    zp.set_kernel_timing(False)
+    assert flags == 0, "unexpected overflow in the benchmark inputs"
+
+    step_ms = elapsed / args.steps * 1e3
+    value = S * args.steps / elapsed
+    bytes_per_elem = 26 + 2 * R
+    alg_bytes = bytes_per_elem * S
+    kern_avg_ms = float(np.mean(kernel_ms))
+    achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(S)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    del st, grads, gather, slot, p0
+    torch.cuda.empty_cache()
+
+    if args.calibration_copy:
+        a = torch.empty(1 << 30, dtype=torch.int16, device=dev)   # 2 GiB
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # a2: bucket pack of the 20,000-tensor stream
+    pack = None
+    if not args.no_pack:
+        pw = W.pack_20k()
+        tensors = W.pack_sources(pw, device=dev)
+        play = zp.partition_layout(pw.numels, pw.n_ranks, stage=2, bucket=pw.bucket)
+        play.bind_tensors(tensors)
+        bucket = torch.empty(pw.bucket, dtype=torch.int16, device=dev)
+        for k in range(pw.n_fills):                                   # warm-up pass
+            play.pack_bucket(k, bucket)
+        torch.cuda.synchronize()
+        zp.set_kernel_timing(True)
+        fill_ms = []
+        t0 = time.perf_counter()
+        for k in range(pw.n_fills):
+            play.pack_bucket(k, bucket)
+            fill_ms.append(zp.last_kernel_ms())
+        torch.cuda.synchronize()
+        pack_wall = time.perf_counter() - t0
+        zp.set_kernel_timing(False)
+        kernel_total = float(np.sum(fill_ms)) * 1e-3
+        pack_bytes = 4 * pw.psi + 2 * (pw.n_fills * pw.bucket - pw.psi)
+        pack_gbs = pack_bytes / kernel_total / 1e9
+        pack = {"workload": "pack_20k: 20,000 fp16 tensors, log-uniform sizes in [1, 2^22], "
+                            "bucket 2^26, 82 fills",
+                "elements": pw.psi, "fills": pw.n_fills,
+                "elements_per_s": round(pw.psi / pack_wall, 1),
+                "ms_total": round(pack_wall * 1e3, 3),
+                "kernel_ms_per_fill": round(kernel_total * 1e3 / pw.n_fills, 4),
+                "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}}
+        play.close()
+        del tensors, bucket
+        torch.cuda.empty_cache()
+
+    # CPU oracle on a bounded sample of the same shard (first step's inputs)
+    cpu = None
+    if cpu_inputs is not None:
+        import oracle
+        p_host, c_host = cpu_inputs
+        ost = oracle.ShardState(p_host)
+        out16 = np.empty(cpu_n, np.uint16)
+        t0 = time.perf_counter()
+        oracle.shard_step(ost, c_host, oracle.LossScaler(w.scale),
+                          oracle.AdamHP(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay), out16)
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(cpu_n / cpu_s, 1), "unit": "elements/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"first {cpu_n} elements of the rank-63 shard, one step "
+                         f"(scalar C oracle, one thread, {cpu_s:.1f} s)"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "zero3_13b: rank 63 of 64, 13B-param GPT-style model "
+                               "(40 layers, hidden 5120, FFN 20480, vocab 50257)",
+                   "shard_elems": S, "contributions": R, "mode": args.mode,
+                   "gather_slots": w.gather_slots, "slot_offset_elems": begin},
+        "algorithmic_gbs_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "kernel_ms": round(kern_avg_ms, 4),
+        "roofline": roofline,
+        "layout_ms": round(layout_ms, 3),
+        "pack": pack,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -236,6 +236,20 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
                     uint16_t* out_slot, void* stream, int32_t* overflow);
 
 /* ------------------------------------------------------------------------ */
+/* Kernel timing (profiling aid)                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Per calling thread.  While enabled (enable != 0), zero_shard_step and
+ * zero_pack_bucket record a HIP event before their first and after their last
+ * device kernel on the call's stream (for zero_shard_step: the fused pass, or
+ * the check and update passes in place; not the flag read-back).
+ * zero_last_kernel_ms waits for the last recorded end event and returns the
+ * elapsed milliseconds.  Errors: STATE (nothing recorded since enabling),
+ * HIP. */
+int zero_set_kernel_timing(int32_t enable);
+int zero_last_kernel_ms(float* ms);
+
+/* ------------------------------------------------------------------------ */
 /* Misc                                                                      */
 /* ------------------------------------------------------------------------ */
 

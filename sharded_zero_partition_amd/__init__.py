@@ -10,7 +10,8 @@ generators; `build` compiles the library.
 """
 
 __all__ = ["partition_layout", "Layout", "ShardState", "shard_step", "AdamHParams",
-           "LossScaler", "ZeroError", "version", "device_info"]
+           "LossScaler", "ZeroError", "version", "device_info", "set_kernel_timing",
+           "last_kernel_ms"]
 
 
 def __getattr__(name):

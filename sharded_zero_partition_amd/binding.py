@@ -100,6 +100,8 @@ SIGNATURES = {
     "zero_layout_bind_tensors": (ctypes.c_int, [_P, _P, _P]),
     "zero_pack_bucket": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
     "zero_shard_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
+    "zero_set_kernel_timing": (ctypes.c_int, [_I32]),
+    "zero_last_kernel_ms": (ctypes.c_int, [_P]),
     "zero_version": (ctypes.c_int, []),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_last_hip_error": (ctypes.c_int, []),
@@ -318,3 +320,15 @@ def device_info():
     arch, mem = ctypes.c_int32(), ctypes.c_int64()
     _check(lib.zero_device_info(_ref(arch), _ref(mem)))
     return arch.value, mem.value
+
+
+def set_kernel_timing(enable: bool):
+    """zero_set_kernel_timing for the calling thread."""
+    _check(lib.zero_set_kernel_timing(1 if enable else 0))
+
+
+def last_kernel_ms() -> float:
+    """zero_last_kernel_ms: device time of the last timed call's kernels."""
+    ms = ctypes.c_float()
+    _check(lib.zero_last_kernel_ms(_ref(ms)))
+    return ms.value

@@ -62,6 +62,53 @@ int blocks_per_cu_pack() {
 
 namespace {
 
+struct ThreadTiming {
+    bool enabled = false;
+    bool recorded = false;
+    int device = -1;
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+thread_local ThreadTiming g_timing;
+
+void timing_release() {
+    if (g_timing.start) (void)hipEventDestroy(g_timing.start);
+    if (g_timing.stop) (void)hipEventDestroy(g_timing.stop);
+    g_timing.start = g_timing.stop = nullptr;
+    g_timing.device = -1;
+    g_timing.recorded = false;
+}
+
+}  // namespace
+
+hipError_t timing_begin(hipStream_t stream) {
+    if (!g_timing.enabled) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != g_timing.device) {
+        timing_release();
+        e = hipEventCreate(&g_timing.start);
+        if (e == hipSuccess) e = hipEventCreate(&g_timing.stop);
+        if (e != hipSuccess) {
+            timing_release();
+            return e;
+        }
+        g_timing.device = dev;
+    }
+    g_timing.recorded = false;
+    return hipEventRecord(g_timing.start, stream);
+}
+
+hipError_t timing_end(hipStream_t stream) {
+    if (!g_timing.enabled || !g_timing.start) return hipSuccess;
+    hipError_t e = hipEventRecord(g_timing.stop, stream);
+    if (e == hipSuccess) g_timing.recorded = true;
+    return e;
+}
+
+namespace {
+
 // Per-device workspace: the overflow flag word and a pinned host word to read
 // it back into.  Created on a device's first shard step and kept until the
 // process ends; `mu` serialises shard steps on the device (they share the
@@ -224,6 +271,8 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         a.flag = ws->d_flag;
         a.epoch = ws->epoch;
 
+        e = zp::timing_begin(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
         if (pingpong) {
             e = zp::launch_fused_step(a, ws->cu_count, s);
             if (e != hipSuccess) return zp::fail_hip(e, "shard step kernel launch");
@@ -233,6 +282,8 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
             e = zp::launch_update_in_place(a, ws->cu_count, s);
             if (e != hipSuccess) return zp::fail_hip(e, "update kernel launch");
         }
+        e = zp::timing_end(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
         e = hipMemcpyAsync(ws->h_flag, ws->d_flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return zp::fail_hip(e, "reading the overflow flag");
@@ -264,6 +315,23 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         }
     }
     if (overflow) *overflow = flag;
+    return ZERO_OK;
+}
+
+extern "C" int zero_set_kernel_timing(int32_t enable) {
+    zp::clear_error();
+    zp::g_timing.enabled = enable != 0;
+    zp::g_timing.recorded = false;
+    return ZERO_OK;
+}
+
+extern "C" int zero_last_kernel_ms(float* ms) {
+    zp::clear_error();
+    if (!ms) return fail(ZERO_ERR_INVALID_ARG, "ms is NULL");
+    if (!zp::g_timing.recorded) return fail(ZERO_ERR_STATE, "no kernel timed since timing was enabled");
+    hipError_t e = hipEventSynchronize(zp::g_timing.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, zp::g_timing.start, zp::g_timing.stop);
+    if (e != hipSuccess) return zp::fail_hip(e, "reading kernel timing events");
     return ZERO_OK;
 }
 

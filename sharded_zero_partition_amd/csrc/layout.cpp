@@ -387,8 +387,13 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     a.fill_base = fill * l->bucket;
     a.bucket_elems = l->bucket;
     a.bucket = bucket;
-    e = zp::launch_pack(a, l->cu_count, static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    e = zp::timing_begin(st);
+    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+    e = zp::launch_pack(a, l->cu_count, st);
     if (e != hipSuccess) return zp::fail_hip(e, "pack kernel launch");
+    e = zp::timing_end(st);
+    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
     if (packed_elems) *packed_elems = std::min(l->bucket, l->psi - a.fill_base);
     return ZERO_OK;
 }

@@ -90,6 +90,11 @@ hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t
 // a skipped ping-pong step): out16[i] = fp16(p_in[i]).
 hipError_t launch_slot_from_master(const StepLaunch& a, int cu_count, hipStream_t stream);
 
+// Kernel timing (zero_set_kernel_timing): begin/end mark the first and last
+// kernel of a call on its stream; both are no-ops while timing is disabled.
+hipError_t timing_begin(hipStream_t stream);
+hipError_t timing_end(hipStream_t stream);
+
 // Launch shape knobs (blocks per CU of the grid-stride kernels), read once
 // from ZERO_BLOCKS_PER_CU / ZERO_PACK_BLOCKS_PER_CU when set.
 int blocks_per_cu_step();
