@@ -51,12 +51,17 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 }  // namespace
 
 int blocks_per_cu_step() {
-    static const int v = env_int("ZERO_BLOCKS_PER_CU", 8, 1, 64);
+    static const int v = env_int("ZERO_BLOCKS_PER_CU", 8, 1, 4096);
+    return v;
+}
+
+int blocks_per_cu_tiled() {
+    static const int v = env_int("ZERO_TILED_BLOCKS_PER_CU", 1, 1, 4096);
     return v;
 }
 
 int blocks_per_cu_pack() {
-    static const int v = env_int("ZERO_PACK_BLOCKS_PER_CU", 8, 1, 64);
+    static const int v = env_int("ZERO_PACK_BLOCKS_PER_CU", 8, 1, 4096);
     return v;
 }
 

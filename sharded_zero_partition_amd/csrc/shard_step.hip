@@ -189,6 +189,126 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
     if (kFlag) raise_flag(a, bad);
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant for R = 1, 2, 4 (the common counts).
+//
+// Each wave owns 512-element tiles, tile t covering [512 t, 512 t + 512).
+// Lane l holds elements 4l..4l+3 and 256+4l..256+4l+3 of the tile, so every
+// load and store instruction of the wave touches one contiguous 1 KiB (fp32)
+// or 512 B (fp16) range.  The grid is persistent (a few waves per SIMD) and
+// each wave walks its tiles with a register double buffer: the loads of the
+// next tile are in flight while the current tile is computed and stored, so
+// the ALU work overlaps the memory traffic instead of adding to it.
+// ---------------------------------------------------------------------------
+
+constexpr int kTile = 512;
+
+template <int R>
+struct TileRegs {
+    u32x2 g[R][2];   // 4 fp16 values per half, per contribution
+    f32x4 p[2], m[2], v[2];
+};
+
+template <int R>
+__device__ __forceinline__ void load_tile(const StepLaunch& a, int64_t base, int lane,
+                                          TileRegs<R>& t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t e = base + h * 256 + 4 * lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            t.g[r][h] = load_stream(reinterpret_cast<const u32x2*>(a.grad[r] + e));
+        t.p[h] = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e));
+        t.m[h] = load_stream(reinterpret_cast<const f32x4*>(a.m_in + e));
+        t.v[h] = load_stream(reinterpret_cast<const f32x4*>(a.v_in + e));
+    }
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_half4(uint16_t* dst, const float p[4]) {
+    const uint32_t w0 = f2h(p[0]) | (f2h(p[1]) << 16);
+    const uint32_t w1 = f2h(p[2]) | (f2h(p[3]) << 16);
+    if (OUT == kOut16B || OUT == kOut8B) {
+        store_stream(reinterpret_cast<u32x2*>(dst), u32x2{w0, w1});
+    } else if (OUT == kOut4B) {
+        store_stream(reinterpret_cast<uint32_t*>(dst), w0);
+        store_stream(reinterpret_cast<uint32_t*>(dst + 2), w1);
+    } else {
+        dst[0] = uint16_t(w0);
+        dst[1] = uint16_t(w0 >> 16);
+        dst[2] = uint16_t(w1);
+        dst[3] = uint16_t(w1 >> 16);
+    }
+}
+
+template <int R, int OUT, bool kFlag>
+__device__ __forceinline__ void compute_tile(const StepLaunch& a, int64_t base, int lane,
+                                             const TileRegs<R>& t, bool& bad) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t e = base + h * 256 + 4 * lane;
+        float s[4];
+        const uint32_t w0[2] = {t.g[0][h].x, t.g[0][h].y};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s[k] = h2f(w0[k >> 1] >> (16 * (k & 1)));
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            const uint32_t w[2] = {t.g[r][h].x, t.g[r][h].y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s[k] = s[k] + h2f(w[k >> 1] >> (16 * (k & 1)));
+        }
+        float p[4] = {t.p[h].x, t.p[h].y, t.p[h].z, t.p[h].w};
+        float m[4] = {t.m[h].x, t.m[h].y, t.m[h].z, t.m[h].w};
+        float v[4] = {t.v[h].x, t.v[h].y, t.v[h].z, t.v[h].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (kFlag) bad |= not_finite(s[k]);
+            adam_element(a, s[k], p[k], m[k], v[k]);
+        }
+        store_stream(reinterpret_cast<f32x4*>(a.p_out + e), f32x4{p[0], p[1], p[2], p[3]});
+        store_stream(reinterpret_cast<f32x4*>(a.m_out + e), f32x4{m[0], m[1], m[2], m[3]});
+        store_stream(reinterpret_cast<f32x4*>(a.v_out + e), f32x4{v[0], v[1], v[2], v[3]});
+        store_half4<OUT>(a.out16 + e, p);
+    }
+}
+
+template <int R, int OUT, bool kFlag, bool kSkip>
+__global__ __launch_bounds__(kThreads) void step_kernel_tiled(const StepLaunch a) {
+    if (kSkip && __atomic_load_n(a.flag, __ATOMIC_RELAXED) == a.epoch) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t ntiles = a.n / kTile;
+    const int64_t waves = int64_t(gridDim.x) * (kThreads / 64);
+    int64_t t = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+    bool bad = false;
+    TileRegs<R> A, B;
+    if (t < ntiles) load_tile<R>(a, t * kTile, lane, A);
+    while (t < ntiles) {
+        int64_t tn = t + waves;
+        if (tn < ntiles) load_tile<R>(a, tn * kTile, lane, B);
+        compute_tile<R, OUT, kFlag>(a, t * kTile, lane, A, bad);
+        t = tn;
+        if (t >= ntiles) break;
+        tn = t + waves;
+        if (tn < ntiles) load_tile<R>(a, tn * kTile, lane, A);
+        compute_tile<R, OUT, kFlag>(a, t * kTile, lane, B, bad);
+        t = tn;
+    }
+    // the last S mod 512 elements: block 0, one element per thread per pass
+    if (blockIdx.x == 0) {
+        for (int64_t e = ntiles * kTile + threadIdx.x; e < a.n; e += kThreads) {
+            const float s = reduce1<R>(a, e);
+            if (kFlag) bad |= not_finite(s);
+            float p = a.p_in[e], m = a.m_in[e], v = a.v_in[e];
+            adam_element(a, s, p, m, v);
+            a.p_out[e] = p;
+            a.m_out[e] = m;
+            a.v_out[e] = v;
+            a.out16[e] = uint16_t(f2h(p));
+        }
+    }
+    if (kFlag) raise_flag(a, bad);
+}
+
 // In-place pass 1: overflow check over the contributions alone.  A sum of at
 // most 16 finite fp16 values is finite in fp32 (16 * 65504 << FLT_MAX), and
 // inf or NaN in any input makes the fp32 sum inf or NaN, so "some sum is not
@@ -261,6 +381,22 @@ dim3 grid_for(int64_t n, int cu_count, int per_cu) {
 }
 
 template <bool kFlag, bool kSkip, int R>
+void launch_tiled_r(const StepLaunch& a, int cu_count, hipStream_t s) {
+    const int64_t ntiles = a.n / kTile;
+    int64_t blocks = (ntiles + 3) / 4;
+    const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * blocks_per_cu_tiled();
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;   // block 0 also owns the tail
+    const dim3 grid{unsigned(blocks)};
+    switch (out_class(a.out16)) {
+        case kOut16B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut8B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut4B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_kernel_tiled<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+    }
+}
+
+template <bool kFlag, bool kSkip, int R>
 void launch_step_r(const StepLaunch& a, dim3 grid, hipStream_t s) {
     switch (out_class(a.out16)) {
         case kOut16B: hipLaunchKernelGGL((step_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
@@ -271,11 +407,12 @@ void launch_step_r(const StepLaunch& a, dim3 grid, hipStream_t s) {
 }
 
 template <bool kFlag, bool kSkip>
-void launch_step(const StepLaunch& a, dim3 grid, hipStream_t s) {
+void launch_step(const StepLaunch& a, int cu_count, hipStream_t s) {
+    const dim3 grid = grid_for(a.n, cu_count, blocks_per_cu_step());
     switch (a.R) {
-        case 1: launch_step_r<kFlag, kSkip, 1>(a, grid, s); break;
-        case 2: launch_step_r<kFlag, kSkip, 2>(a, grid, s); break;
-        case 4: launch_step_r<kFlag, kSkip, 4>(a, grid, s); break;
+        case 1: launch_tiled_r<kFlag, kSkip, 1>(a, cu_count, s); break;
+        case 2: launch_tiled_r<kFlag, kSkip, 2>(a, cu_count, s); break;
+        case 4: launch_tiled_r<kFlag, kSkip, 4>(a, cu_count, s); break;
         default: launch_step_r<kFlag, kSkip, 0>(a, grid, s); break;
     }
 }
@@ -283,12 +420,12 @@ void launch_step(const StepLaunch& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream) {
-    launch_step<true, false>(a, grid_for(a.n, cu_count, blocks_per_cu_step()), stream);
+    launch_step<true, false>(a, cu_count, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t stream) {
-    launch_step<false, true>(a, grid_for(a.n, cu_count, blocks_per_cu_step()), stream);
+    launch_step<false, true>(a, cu_count, stream);
     return hipGetLastError();
 }
 

@@ -96,8 +96,10 @@ hipError_t timing_begin(hipStream_t stream);
 hipError_t timing_end(hipStream_t stream);
 
 // Launch shape knobs (blocks per CU of the grid-stride kernels), read once
-// from ZERO_BLOCKS_PER_CU / ZERO_PACK_BLOCKS_PER_CU when set.
+// from ZERO_BLOCKS_PER_CU / ZERO_TILED_BLOCKS_PER_CU / ZERO_PACK_BLOCKS_PER_CU
+// when set.
 int blocks_per_cu_step();
+int blocks_per_cu_tiled();
 int blocks_per_cu_pack();
 
 }  // namespace zp
