@@ -306,8 +306,9 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
 
     // chunk index: first[c] = source holding flat index c << shift.  The chunk
-    // is at least 4096 elements and grows so that the table stays <= 2^22.
-    int shift = 12;
+    // is at least 2048 elements (one wave span of the pack kernel) and grows
+    // so that the table stays <= 2^22 entries.
+    int shift = 11;
     while (((l->psi + (int64_t(1) << shift) - 1) >> shift) > (int64_t(1) << 22)) ++shift;
     const int64_t n_chunks = (l->psi + (int64_t(1) << shift) - 1) >> shift;
     std::vector<int32_t> first;

@@ -6,17 +6,20 @@
 // the window [k*B, (k+1)*B) of the tensors laid back to back; past the end of
 // the last tensor the bucket holds zeros.  The copy is bitwise.
 //
-// Design: the bucket is cut into 8-element (16-byte) vectors and each thread
-// of a grid-stride loop owns whole vectors, so stores are always aligned
-// 128-bit writes and the work is balanced no matter how ragged the tensors
-// are.  A thread finds the source tensor of its vector with a binary search
-// over a chunk-indexed slice of the (sorted) tensor table.  When the 8
-// elements come from one tensor it reads them with one 128-bit load, or two
-// aligned 128-bit loads and a funnel shift when the source is misaligned
-// (the second load is the neighbour thread's first one, so it hits in
-// cache); vectors that straddle tensors, touch a tensor edge or the end of
-// the stream are gathered element by element.  No LDS: each wave's loads are
-// already contiguous.
+// Design: the bucket is cut into 8-element (16-byte) vectors, so every store
+// is an aligned 128-bit write, and the work is balanced over the bucket no
+// matter how ragged the tensors are.  A wave owns a span of 512 U elements
+// (U = 2) and lane l the vectors at 512 u + 8 l, so each store instruction
+// writes 1 KiB contiguously.  The wave reads the source range of its span
+// from a chunk index built at bind time (chunk = one span), through the
+// scalar cache; when the span lies in one tensor (almost always) no search is
+// needed, otherwise each lane binary-searches the few candidates.  When the
+// 8 elements of a vector come from one tensor the lane reads one aligned
+// 128-bit block, or two and a funnel shift when the source is misaligned
+// (the second block is the neighbour lane's first, so it hits in cache); the
+// loads of all U vectors are issued before any is used.  Vectors that
+// straddle tensors, touch a tensor edge or the end of the stream are gathered
+// element by element.  No LDS: each wave's accesses are already contiguous.
 #include "zp_internal.hpp"
 
 namespace zp {
@@ -52,6 +55,7 @@ __device__ __forceinline__ u32x4 window8(u32x4 a, u32x4 b, int ph) {
     const uint32_t w0 = a.x, w1 = a.y, w2 = a.z, w3 = a.w;
     const uint32_t w4 = b.x, w5 = b.y, w6 = b.z, w7 = b.w;
     switch (ph) {
+        case 0: return a;
         case 1: return u32x4{funnel16(w0, w1), funnel16(w1, w2), funnel16(w2, w3), funnel16(w3, w4)};
         case 2: return u32x4{w1, w2, w3, w4};
         case 3: return u32x4{funnel16(w1, w2), funnel16(w2, w3), funnel16(w3, w4), funnel16(w4, w5)};
@@ -79,39 +83,103 @@ __device__ __forceinline__ u32x4 gather8(const PackSrc* __restrict__ src, int i,
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-__global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackLaunch a) {
-    const int64_t n_vec = (a.bucket_elems + 7) >> 3;
-    const int64_t stride = int64_t(gridDim.x) * kPackThreads;
-    for (int64_t j = int64_t(blockIdx.x) * kPackThreads + threadIdx.x; j < n_vec; j += stride) {
-        const int64_t o = j << 3;
+// Index of the source holding flat index g, searched in [lo, hi] only.
+__device__ __forceinline__ int find_src_in(const PackSrc* __restrict__ src, int lo, int hi,
+                                           int64_t g) {
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (src[mid].flat_off <= g)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Wave-span variant.  Wave w owns bucket elements [w*span, (w+1)*span),
+// span = 512 * U; lane l handles the U vectors at offsets 512 u + 8 l, so
+// each of the U store instructions covers 1 KiB of the bucket contiguously.
+// The wave first resolves the source range of its whole span (the same
+// search on every lane, so it is served by the cache), then every lane
+// finds its own source inside that range -- usually a single candidate --
+// and issues the loads of all U vectors before any of them is used, so a
+// lane keeps up to 2U independent 16-byte loads in flight.
+template <int U>
+__global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunch a) {
+    constexpr int64_t kSpan = 512 * U;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform values live in scalar registers; the table reads below
+    // then go through the scalar cache
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = int64_t(blockIdx.x) * (kPackThreads / 64) + wave_in_block;
+    const int64_t o_wave = wave * kSpan;
+    if (o_wave >= a.bucket_elems) return;   // the whole wave leaves together
+    const int64_t g_wave = a.fill_base + o_wave;
+    int lo = 0, hi = 0;
+    if (g_wave < a.psi) {
+        int64_t g_last = a.fill_base + min(o_wave + kSpan, a.bucket_elems) - 1;
+        if (g_last >= a.psi) g_last = a.psi - 1;
+        // sources of the span lie in [first[chunk(g_wave)], first[chunk(g_last) + 1]]
+        lo = a.first[g_wave >> a.chunk_shift];
+        hi = a.first[(g_last >> a.chunk_shift) + 1];
+    }
+    // when the whole span lies in one tensor (the common case) its table
+    // entry is wave-uniform and read once through the scalar cache
+    const bool one_src = lo == hi;
+    PackSrc uni = {nullptr, 0, 0};
+    if (one_src && g_wave < a.psi) uni = a.src[lo];
+    int src_i[U];
+    int mode[U];                 // 0 zeros, 1 aligned-window loads, 2 element gather
+    const uint16_t* blk[U];      // first aligned 16-byte block
+    int phase[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t o = o_wave + 512 * u + 8 * lane;
         const int64_t g = a.fill_base + o;
+        src_i[u] = lo;
+        mode[u] = 0;
+        blk[u] = nullptr;
+        phase[u] = 0;
+        if (o < a.bucket_elems && g < a.psi) {
+            const int i = one_src ? lo : find_src_in(a.src, lo, hi, g);
+            src_i[u] = i;
+            const PackSrc s = one_src ? uni : a.src[i];
+            const int64_t rel = g - s.flat_off;
+            mode[u] = 2;
+            if (a.bucket_elems - o >= 8 && rel + 8 <= s.len) {
+                const uint16_t* p = s.ptr + rel;
+                const int ph = int((reinterpret_cast<uintptr_t>(p) & 15) >> 1);
+                const uint16_t* base = p - ph;
+                // the blocks read are [base, base + 8) and, when misaligned,
+                // [base + 8, base + 16): both must lie inside the tensor
+                if (ph == 0 || (base >= s.ptr && base + 16 <= s.ptr + s.len)) {
+                    mode[u] = 1;
+                    blk[u] = base;
+                    phase[u] = ph;
+                }
+            }
+        }
+    }
+    u32x4 lo_v[U], hi_v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (mode[u] == 1) {
+            lo_v[u] = *reinterpret_cast<const u32x4*>(blk[u]);
+            // aligned: read the same block twice rather than past its end
+            hi_v[u] = *reinterpret_cast<const u32x4*>(blk[u] + (phase[u] ? 8 : 0));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t o = o_wave + 512 * u + 8 * lane;
+        if (o >= a.bucket_elems) continue;
         const int64_t left = a.bucket_elems - o;
         const int nvalid = left < 8 ? int(left) : 8;
         u32x4 out = u32x4{0u, 0u, 0u, 0u};
-        if (g < a.psi) {
-            const int i = find_src(a.src, a.first, a.chunk_shift, g);
-            const PackSrc s = a.src[i];
-            const int64_t rel = g - s.flat_off;
-            if (nvalid == 8 && rel + 8 <= s.len) {
-                const uint16_t* p = s.ptr + rel;
-                const int ph = int((reinterpret_cast<uintptr_t>(p) & 15) >> 1);
-                if (ph == 0) {
-                    out = *reinterpret_cast<const u32x4*>(p);
-                } else {
-                    // both aligned 16-byte blocks must lie inside the tensor
-                    const uint16_t* base = p - ph;
-                    if (base >= s.ptr && base + 16 <= s.ptr + s.len) {
-                        const u32x4 lo = *reinterpret_cast<const u32x4*>(base);
-                        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + 8);
-                        out = window8(lo, hi, ph);
-                    } else {
-                        out = gather8(a.src, i, g, 8, a.psi);
-                    }
-                }
-            } else {
-                out = gather8(a.src, i, g, nvalid, a.psi);
-            }
-        }
+        if (mode[u] == 1)
+            out = window8(lo_v[u], hi_v[u], phase[u]);
+        else if (mode[u] == 2)
+            out = gather8(a.src, src_i[u], a.fill_base + o, nvalid, a.psi);
         if (nvalid == 8) {
             *reinterpret_cast<u32x4*>(a.bucket + o) = out;
         } else {
@@ -122,15 +190,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackLaunch a) 
     }
 }
 
+constexpr int kPackSpanU = 2;
+
 }  // namespace
 
 hipError_t launch_pack(const PackLaunch& a, int cu_count, hipStream_t stream) {
-    const int64_t n_vec = (a.bucket_elems + 7) >> 3;
-    int64_t blocks = (n_vec + kPackThreads - 1) / kPackThreads;
-    const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * blocks_per_cu_pack();
-    if (blocks > cap) blocks = cap;
+    (void)cu_count;
+    constexpr int64_t kSpan = 512 * kPackSpanU;
+    const int64_t waves = (a.bucket_elems + kSpan - 1) / kSpan;
+    int64_t blocks = (waves + 3) / 4;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(pack_kernel, dim3(unsigned(blocks)), dim3(kPackThreads), 0, stream, a);
+    hipLaunchKernelGGL(pack_span_kernel<kPackSpanU>, dim3(unsigned(blocks)), dim3(kPackThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
