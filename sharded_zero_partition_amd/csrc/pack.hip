@@ -128,6 +128,44 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
     const bool one_src = lo == hi;
     PackSrc uni = {nullptr, 0, 0};
     if (one_src && g_wave < a.psi) uni = a.src[lo];
+
+    // Cooperative path: a full span inside one tensor has one misalignment
+    // phase for the whole wave, so each lane loads a single aligned block and
+    // takes the block after it from the next lane (the last lane of a group
+    // from the next group's first lane, and of the last group from one extra
+    // block read by the whole wave).
+    if (one_src && o_wave + kSpan <= a.bucket_elems && g_wave + kSpan <= a.psi) {
+        const uint16_t* p0 = uni.ptr + (g_wave - uni.flat_off);
+        const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+        const uint16_t* base0 = p0 - ph;
+        const int64_t need = ph ? kSpan + 8 : kSpan;     // elements read from base0 on
+        if (base0 >= uni.ptr && base0 + need <= uni.ptr + uni.len) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = *reinterpret_cast<const u32x4*>(base0 + 512 * u + 8 * lane);
+            u32x4 extra = v[U - 1];
+            if (ph) extra = *reinterpret_cast<const u32x4*>(base0 + kSpan);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                u32x4 nxt;
+                nxt.x = __shfl_down(v[u].x, 1);
+                nxt.y = __shfl_down(v[u].y, 1);
+                nxt.z = __shfl_down(v[u].z, 1);
+                nxt.w = __shfl_down(v[u].w, 1);
+                const u32x4 head = u + 1 < U ? v[u + 1 < U ? u + 1 : u] : extra;
+                u32x4 first_of_next;
+                first_of_next.x = __shfl(head.x, 0);
+                first_of_next.y = __shfl(head.y, 0);
+                first_of_next.z = __shfl(head.z, 0);
+                first_of_next.w = __shfl(head.w, 0);
+                if (lane == 63) nxt = first_of_next;
+                const int64_t o = o_wave + 512 * u + 8 * lane;
+                *reinterpret_cast<u32x4*>(a.bucket + o) = window8(v[u], nxt, ph);
+            }
+            return;
+        }
+    }
     int src_i[U];
     int mode[U];                 // 0 zeros, 1 aligned-window loads, 2 element gather
     const uint16_t* blk[U];      // first aligned 16-byte block
