@@ -70,6 +70,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 2 GiB device copy (scale reference for HBM counters)")
+    ap.add_argument("--pack-views", action="store_true",
+                    help="pack sources as views of one buffer instead of 20,000 allocations")
     return ap.parse_args()
 
 
@@ -168,7 +170,7 @@ def main():
     pack = None
     if not args.no_pack:
         pw = W.pack_20k()
-        tensors = W.pack_sources(pw, device=dev)
+        tensors = W.pack_sources(pw, device=dev, views=args.pack_views)
         play = zp.partition_layout(pw.numels, pw.n_ranks, stage=2, bucket=pw.bucket)
         play.bind_tensors(tensors)
         bucket = torch.empty(pw.bucket, dtype=torch.int16, device=dev)

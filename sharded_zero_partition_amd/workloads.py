@@ -233,13 +233,26 @@ def special_positions(w: ShardWorkload, n: int = None) -> Tuple[np.ndarray, np.n
     return pos.astype(np.int64), vals
 
 
-def pack_sources(w: PackWorkload, device=None):
+def pack_sources(w: PackWorkload, device=None, views: bool = False):
     """The fp16 gradient tensors of the pack workload, N(0, 1e-3), as a list
-    of torch.int16 views on `device`.  Drawn in one flat device array (or
-    host array when small) and split into separately allocated tensors."""
+    of torch.int16 tensors on `device`.  Drawn in one flat array (host array
+    when small) and split into separately allocated tensors, or, with
+    views=True, as views of one freshly drawn buffer with a 1..7-element gap
+    before each tensor (same distribution and alignment mix, and no
+    per-tensor copy at all)."""
     import torch
     out = []
     total = w.psi
+    if views:
+        gaps = host_rng(w.wid, KIND_PACK, 1, 0).integers(1, 8, size=len(w.numels))
+        n_buf = total + int(gaps.sum()) + 8
+        buf = normal_f32(n_buf, 1e-3, w.wid, KIND_PACK, 2, 0, device).to(torch.float16)
+        off = 0
+        for n, gap in zip(w.numels, gaps):
+            off += int(gap)
+            out.append(buf[off:off + n].view(torch.int16))
+            off += n
+        return out
     if total <= HOST_RNG_LIMIT:
         flat = normal_f32(total, 1e-3, w.wid, KIND_PACK, 0, 0).to(torch.float16)
         if device is not None:
