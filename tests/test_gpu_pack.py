@@ -99,3 +99,11 @@ def test_pack_20k_full_size():
     info = _check_all_fills(tensors, w.numels, w.bucket, n_ranks=w.n_ranks)
     assert (info.psi, info.n_fills, info.shard_elems, info.padding) == \
         (5_481_113_944, 82, 342_569_622, 8)
+
+
+def test_pack_20k_views_full_size():
+    """The same stream with every tensor a view into one buffer at a 1..7
+    element gap: all misalignment phases, bit-exact on every fill."""
+    w = W.pack_20k()
+    tensors = W.pack_sources(w, device="cuda", views=True)
+    _check_all_fills(tensors, w.numels, w.bucket, n_ranks=w.n_ranks)

@@ -150,3 +150,24 @@ def test_errors_leave_state_untouched():
         zp.shard_step(st, [g[:S]], hpc, sc, p.view(torch.int16)[:S])   # slot overlaps p
     assert st.t == 0 and sc.scale == 1024.0 and not p.any()
     assert int((slot != SENTINEL).sum()) == 0
+
+
+def test_kernel_timing_api():
+    """zero_set_kernel_timing / zero_last_kernel_ms: STATE before anything is
+    timed, a positive time after a timed step, STATE again once re-enabled."""
+    import sharded_zero_partition_amd as zp
+    rng = np.random.default_rng(13)
+    S = 1 << 20
+    ls = Lockstep(_p0(rng, S), 2, HP, 1024.0, True)
+    zp.set_kernel_timing(True)
+    with pytest.raises(zp.ZeroError, match="STATE"):
+        zp.last_kernel_ms()
+    ls.step(host_contribs(rng, S, 2, 1024.0))
+    ms = zp.last_kernel_ms()
+    assert 0.0 < ms < 1000.0
+    zp.set_kernel_timing(True)
+    with pytest.raises(zp.ZeroError, match="STATE"):
+        zp.last_kernel_ms()
+    zp.set_kernel_timing(False)
+    ls.step(host_contribs(rng, S, 2, 1024.0))      # untimed calls still work
+    assert ls.bit_exact
