@@ -8,7 +8,8 @@ nothing from the product.
 Contents
   layout.py       partition layout, stage memory model, bucket pack (Python)
   zero_oracle.c   fp16 conversions, R-way reduce, overflow flag, Adam (scalar C)
-  (this file)     ctypes wrapper over zero_oracle.c and the loss-scale control
+  (this file)     ctypes wrapper over zero_oracle.c, the loss-scale control and
+                  the bucket reduce-to-owner
 
 Every function follows a passage of the ZeRO explainer page (azimuth.plus,
 "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"); the
@@ -25,7 +26,8 @@ import subprocess
 import numpy as np
 
 from .layout import (KINDS, KIND_BYTES, PARTITIONED, Layout, Segment,  # noqa: F401
-                     pack_fill, partition_layout, stage_bytes_per_rank)
+                     flat_window, owner_range, pack_fill, partition_layout,
+                     stage_bytes_per_rank)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zero_oracle.c")
@@ -198,3 +200,24 @@ def shard_step(state: ShardState, contribs, scaler: LossScaler, hp: AdamHP,
         state.t += 1
     scaler.update(bool(flag))
     return int(flag)
+
+
+def reduce_to_owner(contrib_lists, lay: Layout, fill: int, rank: int):
+    """Reduce-to-owner of bucket fill `fill` for rank `rank`.
+
+    contrib_lists holds R lists of fp16 tensors (uint16 bit patterns), one
+    list per reducing rank, each with the layout's tensor sizes.  For every
+    flat index g of the fill that the rank owns (`owner_range`), the owner's
+    fp16 gradient shard receives fp16(c_0(g) + c_1(g) + ... + c_{R-1}(g)),
+    the sum taken in fp32 left to right and rounded once to fp16 (nearest,
+    ties to even).  This is the local arithmetic of the bucketed
+    reduce-scatter of the Stage 2 (P_os+g) paragraph combined with the
+    constant-size buffer of the ZeRO-R paragraph.
+
+    Returns (offset in the rank's shard of the first element, fp16 values)."""
+    lo, hi = owner_range(lay, fill, rank)
+    if lo >= hi:
+        return 0, np.zeros(0, dtype=np.uint16)
+    windows = [flat_window(lst, lo, hi) for lst in contrib_lists]
+    return lo - rank * lay.shard, float_to_half(reduce(windows))
+

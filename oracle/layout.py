@@ -178,13 +178,10 @@ def stage_bytes_per_rank(psi: int, n_ranks: int, stage: int, align: int = 1) -> 
 # bucket pack
 # ---------------------------------------------------------------------------
 
-def pack_fill(tensors: Sequence[np.ndarray], fill: int, bucket: int) -> np.ndarray:
-    """Fill `fill` of the constant-size bucket: the window
-    [fill*bucket, (fill+1)*bucket) of the concatenation of the fp16 tensors
-    (given as uint16 bit patterns, copied bit for bit), zeros past the end."""
-    lo = fill * bucket
-    hi = lo + bucket
-    out = np.zeros(bucket, dtype=np.uint16)
+def flat_window(tensors: Sequence[np.ndarray], lo: int, hi: int) -> np.ndarray:
+    """Elements [lo, hi) of the concatenation of the tensors (uint16 bit
+    patterns, copied bit for bit); positions past the last tensor are zero."""
+    out = np.zeros(max(0, hi - lo), dtype=np.uint16)
     off = 0
     for t in tensors:
         flat = np.asarray(t).reshape(-1).view(np.uint16)
@@ -194,3 +191,19 @@ def pack_fill(tensors: Sequence[np.ndarray], fill: int, bucket: int) -> np.ndarr
             out[a - lo:b - lo] = flat[a - off:b - off]
         off += flat.size
     return out
+
+
+def pack_fill(tensors: Sequence[np.ndarray], fill: int, bucket: int) -> np.ndarray:
+    """Fill `fill` of the constant-size bucket: the window
+    [fill*bucket, (fill+1)*bucket) of the concatenation of the fp16 tensors
+    (given as uint16 bit patterns, copied bit for bit), zeros past the end."""
+    return flat_window(tensors, fill * bucket, fill * bucket + bucket)
+
+
+def owner_range(lay: Layout, fill: int, rank: int):
+    """Flat range [lo, hi) of fill `fill` that rank `rank` owns (lo >= hi when
+    empty): the intersection of the fill window, the rank's shard and the
+    model (padding is never reduced)."""
+    lo = max(fill * lay.bucket, rank * lay.shard)
+    hi = min((fill + 1) * lay.bucket, (rank + 1) * lay.shard, lay.psi)
+    return lo, hi

@@ -5,7 +5,10 @@
     paragraph), plus the closed forms of the three stages;
   * layout: brute force over every flat index of small random tensor lists,
     and the invariants that make the shards an exact equal partition;
-  * bucket pack: brute force element by element on small inputs.
+  * bucket pack: brute force element by element on small inputs;
+  * bucket reduce-to-owner: brute force element by element (owner, fill and
+    numpy float32/float16 arithmetic), and the pieces over all fills and
+    owners tiling the flat vector with the fp16 of its sum.
 """
 
 import json
@@ -230,3 +233,63 @@ def test_pack_is_bitwise():
     t = [np.array([0x7E01, 0x8000, 0x7C00, 0xFC00, 0x7FFF, 0x0001], dtype=np.uint16)]
     got = OL.pack_fill(t, 0, 8)
     assert got.tolist() == [0x7E01, 0x8000, 0x7C00, 0xFC00, 0x7FFF, 0x0001, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# bucket reduce-to-owner
+# ---------------------------------------------------------------------------
+
+def test_reduce_to_owner_brute_force_small():
+    """Element by element: owner by linear scan of the shards, fill by the
+    bucket window, sum with numpy float32 left to right, rounding with numpy's
+    float16 conversion."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        n_t = int(rng.integers(1, 8))
+        numels = [int(x) for x in rng.choice([0, 1, 3, 8, 9, 40, 130], size=n_t)]
+        R = int(rng.integers(1, 5))
+        lists = [[(rng.standard_normal(n, dtype=np.float32) * 30).astype(np.float16).view(np.uint16)
+                  for n in numels] for _ in range(R)]
+        n_ranks = int(rng.integers(1, 5))
+        bucket = int(rng.choice([1, 5, 16, 64]))
+        lay = OL.partition_layout(numels, n_ranks, stage=2, align=int(rng.choice([1, 4])), bucket=bucket)
+        flats = [np.concatenate(l).view(np.uint16) if numels and sum(numels) else np.zeros(0, np.uint16)
+                 for l in lists]
+        for k in range(lay.n_fills):
+            for r in range(n_ranks):
+                off, vals = oracle.reduce_to_owner(lists, lay, k, r)
+                owned = [g for g in range(lay.psi)
+                         if next(q for q in range(n_ranks) if q * lay.shard <= g < (q + 1) * lay.shard) == r
+                         and k * bucket <= g < (k + 1) * bucket]
+                assert vals.size == len(owned)
+                if owned:
+                    assert off == owned[0] - r * lay.shard
+                for j, g in enumerate(owned):
+                    acc = np.float32(flats[0][g:g + 1].view(np.float16)[0])
+                    for f in flats[1:]:
+                        acc = np.float32(acc + np.float32(f[g:g + 1].view(np.float16)[0]))
+                    want = np.array([acc], np.float32).astype(np.float16).view(np.uint16)[0]
+                    assert vals[j] == want, (trial, k, r, g)
+
+
+def test_reduce_to_owner_tiles_the_whole_vector():
+    """Over all fills and owners the pieces tile [0, psi) exactly and equal the
+    fp16 of the whole-vector fp32 sum."""
+    rng = np.random.default_rng(22)
+    numels = [1000, 3, 0, 777, 4096, 5]
+    R = 3
+    lists = [[(rng.standard_normal(n, dtype=np.float32)).astype(np.float16).view(np.uint16)
+              for n in numels] for _ in range(R)]
+    lay = OL.partition_layout(numels, 6, stage=2, align=8, bucket=300)
+    got = np.full(lay.padded, 0xFFFF, np.uint16)
+    for k in range(lay.n_fills):
+        for r in range(6):
+            off, vals = oracle.reduce_to_owner(lists, lay, k, r)
+            if vals.size:
+                assert (got[r * lay.shard + off: r * lay.shard + off + vals.size] == 0xFFFF).all()
+                got[r * lay.shard + off: r * lay.shard + off + vals.size] = vals
+    assert (got[lay.psi:] == 0xFFFF).all()
+    total = sum(np.concatenate(l).view(np.float16).astype(np.float64) for l in lists)
+    # R = 3 fp32 sums of fp16 values equal the exact sums here (|x| < 8, 11-bit
+    # significands, well inside 24 bits), so one rounding to fp16 is the answer
+    assert np.array_equal(got[:lay.psi], total.astype(np.float16).view(np.uint16))
