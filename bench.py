@@ -13,6 +13,8 @@ A timed step is one zero_shard_step call (fused kernel, overflow read-back,
 loss-scale control).  The same run also reports
   * the partition layout of the 484-tensor model (host, once per model),
   * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
+  * the owners' share of the bucketed reduce of two ranks' copies of that
+    stream into the 16 owners' fp16 gradient shards,
   * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
     HIP-event time on its stream) and, when the counter profile under
     profiles/ was taken from the current kernel source, its measured traffic,
@@ -168,6 +170,7 @@ def main():
 
     # a2: bucket pack of the 20,000-tensor stream
     pack = None
+    reduce_owner = None
     if not args.no_pack:
         pw = W.pack_20k()
         tensors = W.pack_sources(pw, device=dev, views=args.pack_views)
@@ -198,7 +201,43 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}}
         play.close()
-        del tensors, bucket
+        del bucket
+
+        # NEXT: the owners' share of the bucketed reduce of two ranks' gradient
+        # tensors (this stream and a second draw), every fill and owner
+        lists = [tensors, W.pack_sources(pw, device=dev, views=args.pack_views, draw=1)]
+        rlay = zp.partition_layout(pw.numels, pw.n_ranks, stage=2, bucket=pw.bucket)
+        rlay.bind_contributions(lists)
+        S4 = rlay.info.shard_elems
+        flat = torch.empty(pw.n_ranks * S4, dtype=torch.int16, device=dev)
+        pairs = [(k, r) for k in range(pw.n_fills) for r in range(pw.n_ranks)
+                 if max(k * pw.bucket, r * S4) < min((k + 1) * pw.bucket, (r + 1) * S4, pw.psi)]
+        for k, r in pairs:                                             # warm-up pass
+            rlay.reduce_to_owner(k, r, flat[r * S4:(r + 1) * S4])
+        torch.cuda.synchronize()
+        zp.set_kernel_timing(True)
+        red_ms = []
+        t0 = time.perf_counter()
+        for k, r in pairs:
+            rlay.reduce_to_owner(k, r, flat[r * S4:(r + 1) * S4])
+            red_ms.append(zp.last_kernel_ms())
+        torch.cuda.synchronize()
+        red_wall = time.perf_counter() - t0
+        zp.set_kernel_timing(False)
+        red_kernel = float(np.sum(red_ms)) * 1e-3
+        red_bytes = 6 * pw.psi                        # 2 x 2 B read + 2 B written
+        red_gbs = red_bytes / red_kernel / 1e9
+        reduce_owner = {
+            "workload": "pack_20k stream, R = 2 ranks' gradient tensors, reduced into the "
+                        "fp16 gradient shards of its 16 owners, all 82 fills",
+            "elements": pw.psi, "launches": len(pairs),
+            "elements_per_s": round(pw.psi / red_wall, 1),
+            "ms_total": round(red_wall * 1e3, 3),
+            "kernel_ms_total": round(red_kernel * 1e3, 3),
+            "roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(red_gbs / HBM_PEAK_GBS, 4)}}
+        rlay.close()
+        del tensors, lists, flat
         torch.cuda.empty_cache()
 
     # CPU oracle on a bounded sample of the same shard (first step's inputs)
@@ -239,6 +278,7 @@ def main():
         "roofline": roofline,
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
+        "reduce_to_owner": reduce_owner,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

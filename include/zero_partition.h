@@ -166,6 +166,38 @@ int zero_pack_bucket(const zero_layout* layout, int64_t fill, uint16_t* bucket,
                      void* stream, int64_t* packed_elems);
 
 /* ------------------------------------------------------------------------ */
+/* Bucket reduce-to-owner (Stage 2 paragraph with the constant-size buffer)  */
+/* ------------------------------------------------------------------------ */
+
+/* Record R lists of device tensors, one list per reducing rank, each with
+ * the layout's tensor sizes in list order, for zero_reduce_to_owner.
+ *   R         1..16
+ *   dev_ptrs  host array of R * n_tensors device pointers to fp16 data; row r
+ *             (entries r*n_tensors ... r*n_tensors + n_tensors - 1) holds rank
+ *             r's tensors; each 2-byte aligned; NULL allowed for empty ones.
+ * Uploads the tables on the current device (the call waits for the upload).
+ * The tensors must stay allocated while the layout reduces.  Binding again
+ * replaces the previous contribution table; the pack binding is separate.
+ * Errors: STATE (no bucket plan), INVALID_ARG, ALIGNMENT, HIP, OUT_OF_MEMORY. */
+int zero_layout_bind_contributions(zero_layout* layout, int32_t R,
+                                   const uint16_t* const* dev_ptrs, void* stream);
+
+/* Owner's share of the reduce of bucket fill `fill`: for every flat index g
+ * with fill*B <= g < (fill+1)*B, rank*S <= g < (rank+1)*S and g < psi,
+ *   shard[g - rank*S] = fp16( c_0(g) + c_1(g) + ... + c_{R-1}(g) )
+ * where c_r is rank r's bound tensor list laid back to back in list order,
+ * the sum is formed in fp32 from contribution 0 up and rounded once to fp16
+ * (nearest, ties to even).  Every other element of `shard` is left as it is.
+ *   shard    device, the owner's fp16 gradient shard (S values), 2-byte aligned
+ *   written  optional host output: elements written (0 when the fill and the
+ *            rank's shard do not meet)
+ * Asynchronous on `stream`; must run on the device the contributions were
+ * bound on.  Errors: STATE (no bucket plan, not bound, another device),
+ * INVALID_ARG (fill or rank out of range), ALIGNMENT, HIP. */
+int zero_reduce_to_owner(const zero_layout* layout, int64_t fill, int32_t rank,
+                         uint16_t* shard, void* stream, int64_t* written);
+
+/* ------------------------------------------------------------------------ */
 /* Fused shard step (Stage 1/2/3 paragraphs: the rank's own partition)        */
 /* ------------------------------------------------------------------------ */
 
@@ -239,8 +271,9 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
 /* Kernel timing (profiling aid)                                            */
 /* ------------------------------------------------------------------------ */
 
-/* Per calling thread.  While enabled (enable != 0), zero_shard_step and
- * zero_pack_bucket record a HIP event before their first and after their last
+/* Per calling thread.  While enabled (enable != 0), zero_shard_step,
+ * zero_pack_bucket and zero_reduce_to_owner record a HIP event before their
+ * first and after their last
  * device kernel on the call's stream (for zero_shard_step: the fused pass, or
  * the check and update passes in place; not the flag read-back).
  * zero_last_kernel_ms waits for the last recorded end event and returns the

@@ -99,6 +99,8 @@ SIGNATURES = {
     "zero_layout_fill_segments": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
     "zero_layout_bind_tensors": (ctypes.c_int, [_P, _P, _P]),
     "zero_pack_bucket": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
+    "zero_layout_bind_contributions": (ctypes.c_int, [_P, _I32, _P, _P]),
+    "zero_reduce_to_owner": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "zero_shard_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
     "zero_set_kernel_timing": (ctypes.c_int, [_I32]),
     "zero_last_kernel_ms": (ctypes.c_int, [_P]),
@@ -234,6 +236,32 @@ class Layout:
         n = ctypes.c_int64()
         _check(lib.zero_pack_bucket(self._h, int(fill), ctypes.c_void_p(_dev_ptr(bucket, "bucket", 2)),
                                     _stream_ptr(stream), _ref(n)))
+        return n.value
+
+
+    def bind_contributions(self, lists, stream=None):
+        """Bind R lists of device fp16 tensors (one list per reducing rank, in
+        the layout's tensor order) for reduce_to_owner."""
+        R = len(lists)
+        nt = self.info.n_tensors
+        ptrs = (ctypes.c_void_p * max(1, R * nt))()
+        for r, lst in enumerate(lists):
+            if len(lst) != nt:
+                raise ValueError(f"list {r} has {len(lst)} tensors, the layout {nt}")
+            for i, t in enumerate(lst):
+                ptrs[r * nt + i] = _dev_ptr(t, f"tensor {r}/{i}", 2) if t.numel() > 0 else None
+        _check(lib.zero_layout_bind_contributions(self._h, R, ptrs, _stream_ptr(stream)))
+        self._contrib = [list(lst) for lst in lists]
+
+    def reduce_to_owner(self, fill: int, rank: int, shard, stream=None) -> int:
+        """Write rank `rank`'s share of fill `fill` of the reduce into its fp16
+        gradient shard (S two-byte elements); returns the elements written."""
+        if shard.numel() != self.info.shard_elems:
+            raise ValueError("shard must hold shard_elems elements")
+        n = ctypes.c_int64()
+        _check(lib.zero_reduce_to_owner(self._h, int(fill), int(rank),
+                                        ctypes.c_void_p(_dev_ptr(shard, "shard", 2)),
+                                        _stream_ptr(stream), _ref(n)))
         return n.value
 
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero_partition.so")
 
-SOURCES = ["layout.cpp", "capi.cpp", "pack.hip", "shard_step.hip"]
+SOURCES = ["layout.cpp", "capi.cpp", "pack.hip", "shard_step.hip", "reduce_owner.hip"]
 
 ARCH = "gfx950"
 

@@ -39,6 +39,16 @@ struct zero_layout {
     int32_t n_src = 0;
     int32_t chunk_shift = 0;
     int cu_count = 0;
+
+    // device tables of the reduce-to-owner (zero_layout_bind_contributions)
+    int r_device = -1;
+    int32_t r_ranks = 0;
+    int32_t r_nsrc = 0;
+    int32_t r_shift = 0;
+    int64_t* d_roff = nullptr;
+    int64_t* d_rlen = nullptr;
+    const uint16_t** d_rptr = nullptr;
+    int32_t* d_rfirst = nullptr;
 };
 
 namespace {
@@ -55,6 +65,45 @@ void free_device_tables(zero_layout* l) {
     l->d_first = nullptr;
     l->device = -1;
     l->n_src = 0;
+}
+
+void free_reduce_tables(zero_layout* l) {
+    void* bufs[4] = {l->d_roff, l->d_rlen, l->d_rptr, l->d_rfirst};
+    for (void* b : bufs)
+        if (b) (void)hipFree(b);
+    l->d_roff = nullptr;
+    l->d_rlen = nullptr;
+    l->d_rptr = nullptr;
+    l->d_rfirst = nullptr;
+    l->r_device = -1;
+    l->r_ranks = 0;
+    l->r_nsrc = 0;
+}
+
+// Chunk index over the flat stream: first[c] = index (among the non-empty
+// tensors, whose flat offsets are `offs`, ascending) of the tensor holding
+// flat index c << shift; first[n_chunks] = last tensor.  The chunk is at
+// least 2048 elements (one wave span) and grows so that the table stays
+// <= 2^22 entries.
+bool chunk_index(const std::vector<int64_t>& offs, int64_t psi, int* shift_out,
+                 std::vector<int32_t>* first) {
+    int shift = 11;
+    while (((psi + (int64_t(1) << shift) - 1) >> shift) > (int64_t(1) << 22)) ++shift;
+    const int64_t n_chunks = (psi + (int64_t(1) << shift) - 1) >> shift;
+    try {
+        first->assign(size_t(n_chunks) + 1, 0);
+    } catch (...) {
+        return false;
+    }
+    size_t s = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        const int64_t g = c << shift;
+        while (s + 1 < offs.size() && offs[s + 1] <= g) ++s;
+        (*first)[size_t(c)] = int32_t(s);
+    }
+    (*first)[size_t(n_chunks)] = offs.empty() ? 0 : int32_t(offs.size() - 1);
+    *shift_out = shift;
+    return true;
 }
 
 // End of the segment starting at flat index cur inside a tensor ending at
@@ -176,6 +225,7 @@ extern "C" int zero_layout_destroy(zero_layout* layout) {
     zp::clear_error();
     if (!layout) return ZERO_OK;
     free_device_tables(layout);
+    free_reduce_tables(layout);
     delete layout;
     return ZERO_OK;
 }
@@ -305,25 +355,17 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     if (src.size() > size_t(std::numeric_limits<int32_t>::max()))
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
 
-    // chunk index: first[c] = source holding flat index c << shift.  The chunk
-    // is at least 2048 elements (one wave span of the pack kernel) and grows
-    // so that the table stays <= 2^22 entries.
-    int shift = 11;
-    while (((l->psi + (int64_t(1) << shift) - 1) >> shift) > (int64_t(1) << 22)) ++shift;
-    const int64_t n_chunks = (l->psi + (int64_t(1) << shift) - 1) >> shift;
+    std::vector<int64_t> offs;
     std::vector<int32_t> first;
+    int shift = 0;
     try {
-        first.resize(size_t(n_chunks) + 1);
+        offs.reserve(src.size());
+        for (const auto& x : src) offs.push_back(x.flat_off);
     } catch (...) {
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
     }
-    size_t s = 0;
-    for (int64_t c = 0; c < n_chunks; ++c) {
-        const int64_t g = c << shift;
-        while (s + 1 < src.size() && src[s + 1].flat_off <= g) ++s;
-        first[size_t(c)] = int32_t(s);
-    }
-    first[size_t(n_chunks)] = src.empty() ? 0 : int32_t(src.size() - 1);
+    if (!chunk_index(offs, l->psi, &shift, &first))
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -396,5 +438,129 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     e = zp::timing_end(st);
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");
     if (packed_elems) *packed_elems = std::min(l->bucket, l->psi - a.fill_base);
+    return ZERO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// bucket reduce-to-owner: device tables and launch
+// ---------------------------------------------------------------------------
+
+extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
+                                              const uint16_t* const* dev_ptrs, void* stream) {
+    zp::clear_error();
+    if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (R < 1 || R > zp::kMaxReduceRanks) return zp::fail(ZERO_ERR_INVALID_ARG, "R must be in 1..16");
+    const size_t nt = l->numel.size();
+    if (nt > 0 && !dev_ptrs) return zp::fail(ZERO_ERR_INVALID_ARG, "dev_ptrs is NULL");
+
+    std::vector<int64_t> offs, lens;
+    std::vector<const uint16_t*> ptrs;
+    std::vector<int32_t> first;
+    int shift = 0;
+    try {
+        for (size_t i = 0; i < nt; ++i) {
+            if (l->numel[i] == 0) continue;
+            offs.push_back(l->offset[i]);
+            lens.push_back(l->numel[i]);
+        }
+        ptrs.reserve(size_t(R) * offs.size());
+        for (int32_t r = 0; r < R; ++r) {
+            for (size_t i = 0; i < nt; ++i) {
+                if (l->numel[i] == 0) continue;
+                const uint16_t* p = dev_ptrs[size_t(r) * nt + i];
+                if (!p) return zp::fail(ZERO_ERR_INVALID_ARG, "NULL pointer for a non-empty tensor");
+                if (reinterpret_cast<uintptr_t>(p) & 1)
+                    return zp::fail(ZERO_ERR_ALIGNMENT, "tensor pointer not 2-byte aligned");
+                ptrs.push_back(p);
+            }
+        }
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
+    if (offs.size() > size_t(std::numeric_limits<int32_t>::max()))
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
+    if (!chunk_index(offs, l->psi, &shift, &first))
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    const size_t n = std::max<size_t>(1, offs.size());
+    void* d[4] = {nullptr, nullptr, nullptr, nullptr};
+    const size_t bytes[4] = {n * sizeof(int64_t), n * sizeof(int64_t),
+                             std::max<size_t>(1, ptrs.size()) * sizeof(void*),
+                             first.size() * sizeof(int32_t)};
+    for (int k = 0; k < 4 && e == hipSuccess; ++k) e = hipMalloc(&d[k], bytes[k]);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const void* host[4] = {offs.data(), lens.data(), ptrs.data(), first.data()};
+    const size_t used[4] = {offs.size() * sizeof(int64_t), lens.size() * sizeof(int64_t),
+                            ptrs.size() * sizeof(void*), first.size() * sizeof(int32_t)};
+    for (int k = 0; k < 4 && e == hipSuccess; ++k)
+        if (used[k]) e = hipMemcpyAsync(d[k], host[k], used[k], hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        for (void* b : d)
+            if (b) (void)hipFree(b);
+        return zp::fail_hip(e, "uploading reduce tables");
+    }
+    free_reduce_tables(l);
+    l->d_roff = static_cast<int64_t*>(d[0]);
+    l->d_rlen = static_cast<int64_t*>(d[1]);
+    l->d_rptr = static_cast<const uint16_t**>(d[2]);
+    l->d_rfirst = static_cast<int32_t*>(d[3]);
+    l->r_ranks = R;
+    l->r_nsrc = int32_t(offs.size());
+    l->r_shift = shift;
+    l->r_device = dev;
+    return ZERO_OK;
+}
+
+extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t rank,
+                                    uint16_t* shard, void* stream, int64_t* written) {
+    zp::clear_error();
+    if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (l->r_device < 0)
+        return zp::fail(ZERO_ERR_STATE, "contributions not bound (zero_layout_bind_contributions)");
+    if (fill < 0 || fill >= l->n_fills) return zp::fail(ZERO_ERR_INVALID_ARG, "fill out of range");
+    if (rank < 0 || rank >= l->n_ranks) return zp::fail(ZERO_ERR_INVALID_ARG, "rank out of range");
+    if (!shard) return zp::fail(ZERO_ERR_INVALID_ARG, "shard is NULL");
+    if (reinterpret_cast<uintptr_t>(shard) & 1)
+        return zp::fail(ZERO_ERR_ALIGNMENT, "shard not 2-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    if (dev != l->r_device) return zp::fail(ZERO_ERR_STATE, "contributions were bound on another device");
+
+    // [fill*B, (fill+1)*B) meets [rank*S, (rank+1)*S) and [0, psi)
+    const int64_t fill_lo = fill * l->bucket;                        // < psi
+    const int64_t fill_hi = (l->bucket >= l->psi - fill_lo) ? l->psi : fill_lo + l->bucket;
+    const int64_t rank_lo = int64_t(rank) * l->shard;
+    const int64_t rank_hi = rank_lo + l->shard;
+    const int64_t g_lo = std::max(fill_lo, rank_lo);
+    const int64_t g_hi = std::min(std::min(fill_hi, rank_hi), l->psi);
+    if (written) *written = g_hi > g_lo ? g_hi - g_lo : 0;
+    if (g_hi <= g_lo) return ZERO_OK;
+
+    zp::ReduceLaunch a;
+    a.off = l->d_roff;
+    a.len = l->d_rlen;
+    a.ptr = l->d_rptr;
+    a.first = l->d_rfirst;
+    a.n_src = l->r_nsrc;
+    a.chunk_shift = l->r_shift;
+    a.R = l->r_ranks;
+    a.g_lo = g_lo;
+    a.g_hi = g_hi;
+    a.base = rank_lo;
+    a.shard = shard;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    e = zp::timing_begin(st);
+    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+    e = zp::launch_reduce_owner(a, st);
+    if (e != hipSuccess) return zp::fail_hip(e, "reduce kernel launch");
+    e = zp::timing_end(st);
+    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
     return ZERO_OK;
 }

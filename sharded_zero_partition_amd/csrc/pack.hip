@@ -20,12 +20,11 @@
 // loads of all U vectors are issued before any is used.  Vectors that
 // straddle tensors, touch a tensor edge or the end of the stream are gathered
 // element by element.  No LDS: each wave's accesses are already contiguous.
+#include "vec16.hpp"
 #include "zp_internal.hpp"
 
 namespace zp {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPackThreads = 256;
 
@@ -44,26 +43,6 @@ __device__ __forceinline__ int find_src(const PackSrc* __restrict__ src,
             hi = mid - 1;
     }
     return lo;
-}
-
-__device__ __forceinline__ uint32_t funnel16(uint32_t lo, uint32_t hi) {
-    return (lo >> 16) | (hi << 16);
-}
-
-// Elements ph .. ph+7 of the 16 elements held in a (0..7) and b (8..15).
-__device__ __forceinline__ u32x4 window8(u32x4 a, u32x4 b, int ph) {
-    const uint32_t w0 = a.x, w1 = a.y, w2 = a.z, w3 = a.w;
-    const uint32_t w4 = b.x, w5 = b.y, w6 = b.z, w7 = b.w;
-    switch (ph) {
-        case 0: return a;
-        case 1: return u32x4{funnel16(w0, w1), funnel16(w1, w2), funnel16(w2, w3), funnel16(w3, w4)};
-        case 2: return u32x4{w1, w2, w3, w4};
-        case 3: return u32x4{funnel16(w1, w2), funnel16(w2, w3), funnel16(w3, w4), funnel16(w4, w5)};
-        case 4: return u32x4{w2, w3, w4, w5};
-        case 5: return u32x4{funnel16(w2, w3), funnel16(w3, w4), funnel16(w4, w5), funnel16(w5, w6)};
-        case 6: return u32x4{w3, w4, w5, w6};
-        default: return u32x4{funnel16(w3, w4), funnel16(w4, w5), funnel16(w5, w6), funnel16(w6, w7)};
-    }
 }
 
 // Element-by-element gather of up to nvalid elements from flat index g on,

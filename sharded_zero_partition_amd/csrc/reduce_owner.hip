@@ -1,0 +1,151 @@
+// reduce_owner.hip -- the owner's share of a bucketed gradient reduce, gfx950.
+//
+// In Stage 2 (P_os+g) of the ZeRO explainer page ("ZeRO: Memory Optimizations
+// Toward Training Trillion Parameter Models", azimuth.plus) every rank ends up
+// with only the reduced gradients of the partition it owns, and the ZeRO-R
+// constant-size buffers paragraph streams the gradients through a fixed-size
+// bucket.  This kernel is the local arithmetic of that exchange for one fill of
+// the bucket and one owner: for each flat index g of the fill that the owner's
+// shard holds, it sums the R ranks' fp16 values in fp32 (rank 0 first) and
+// writes fp16(sum) into the owner's fp16 gradient shard.  The inputs are the R
+// ranks' ragged gradient tensors themselves, so the pack and the reduce happen
+// in one pass without materialising R buckets.
+//
+// Layout of the work: the owner's shard is cut into 8-element vectors on its
+// own 16-byte grid, so every full vector is one aligned 128-bit store.  A wave
+// owns 2 x 64 consecutive vectors (two 1 KiB store groups).  It reads the
+// source range of its span from the chunk index built at bind time; when the
+// span lies inside one tensor the tensor's offset, length and R addresses are
+// wave-uniform (scalar loads).  For each vector whose 8 elements lie in one
+// tensor, each contribution is read as aligned 16-byte blocks (funnel-shifted
+// when misaligned); vectors at the range ends or across tensor boundaries go
+// element by element.  HBM bytes per element: 2R read + 2 written.
+#include "vec16.hpp"
+#include "zp_internal.hpp"
+
+namespace zp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kU = 2;                     // vectors per lane
+constexpr int64_t kSpanVec = 64 * kU;     // vectors per wave
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(x)));
+}
+
+// Last index i in [lo, hi] with off[i] <= g.
+__device__ __forceinline__ int search(const int64_t* __restrict__ off, int lo, int hi, int64_t g) {
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= g)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// fp32 sum over the contributions of the element at offset rel of source i.
+template <int R>
+__device__ __forceinline__ float sum1(const ReduceLaunch& a, int i, int64_t rel) {
+    const int nr = R == 0 ? a.R : R;   // compile-time count unrolls fully
+    float s = h2f(a.ptr[i][rel]);
+    for (int r = 1; r < nr; ++r) s = s + h2f(a.ptr[int64_t(r) * a.n_src + i][rel]);
+    return s;
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaunch a) {
+    const int nr = R == 0 ? a.R : R;   // contributions; compile-time unless R == 0
+    const int lane = threadIdx.x & 63;
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wave_in_block;
+    // vector k covers shard positions [8k - mis, 8k - mis + 8)
+    const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
+    const int64_t j_lo = a.g_lo - a.base;
+    const int64_t j_hi = a.g_hi - a.base;
+    const int64_t k_lo = (j_lo + mis) >> 3;
+    const int64_t k_end = ((j_hi - 1 + mis) >> 3) + 1;
+    const int64_t kw = k_lo + wave * kSpanVec;
+    if (kw >= k_end) return;   // the whole wave leaves together
+
+    // sources of the wave's flat range
+    const int64_t k_last = min(kw + kSpanVec, k_end) - 1;
+    const int64_t jf = max(kw * 8 - mis, j_lo);
+    const int64_t jl = min(k_last * 8 - mis + 8, j_hi) - 1;
+    const int lo = a.first[(a.base + jf) >> a.chunk_shift];
+    const int hi = a.first[((a.base + jl) >> a.chunk_shift) + 1];
+    const bool one = lo == hi;
+    int64_t one_off = 0, one_len = 0;
+    if (one) {
+        one_off = a.off[lo];
+        one_len = a.len[lo];
+    }
+
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t k = kw + 64 * u + lane;
+        if (k >= k_end) continue;
+        const int64_t jv = k * 8 - mis;
+        const int64_t g0 = a.base + jv;
+        if (jv >= j_lo && jv + 8 <= j_hi) {
+            const int i = one ? lo : search(a.off, lo, hi, g0);
+            const int64_t soff = one ? one_off : a.off[i];
+            const int64_t slen = one ? one_len : a.len[i];
+            const int64_t rel = g0 - soff;
+            if (rel + 8 <= slen) {
+                float s[8];
+                for (int r = 0; r < nr; ++r) {
+                    const uint16_t* t = a.ptr[int64_t(r) * a.n_src + i];
+                    const u32x4 v = load8(t + rel, t, t + slen);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
+                        s[e] = r == 0 ? x : s[e] + x;
+                    }
+                }
+                uint32_t o[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = f2h(s[2 * d]) | (f2h(s[2 * d + 1]) << 16);
+                *reinterpret_cast<u32x4*>(a.shard + jv) = u32x4{o[0], o[1], o[2], o[3]};
+                continue;
+            }
+        }
+        // range ends and tensor boundaries: element by element
+        for (int e = 0; e < 8; ++e) {
+            const int64_t j = jv + e;
+            if (j < j_lo || j >= j_hi) continue;
+            const int64_t g = a.base + j;
+            const int i = search(a.off, lo, hi, g);
+            a.shard[j] = uint16_t(f2h(sum1<R>(a, i, g - a.off[i])));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream) {
+    const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
+    const int64_t j_lo = a.g_lo - a.base;
+    const int64_t j_hi = a.g_hi - a.base;
+    const int64_t nvec = ((j_hi - 1 + mis) >> 3) + 1 - ((j_lo + mis) >> 3);
+    const int64_t waves = (nvec + kSpanVec - 1) / kSpanVec;
+    int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    if (blocks < 1) blocks = 1;
+    const dim3 grid{unsigned(blocks)};
+    switch (a.R) {
+        case 1: hipLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(reduce_owner_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(reduce_owner_kernel<0>, grid, dim3(kThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace zp

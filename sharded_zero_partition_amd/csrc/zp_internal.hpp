@@ -45,6 +45,28 @@ struct PackLaunch {
 hipError_t launch_pack(const PackLaunch& a, int cu_count, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
+// bucket reduce-to-owner
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxReduceRanks = 16;
+
+struct ReduceLaunch {
+    const int64_t* off;          // device, n_src flat offsets (sorted)
+    const int64_t* len;          // device, n_src lengths (> 0)
+    const uint16_t* const* ptr;  // device, R * n_src addresses, row r = rank r
+    const int32_t* first;        // device chunk index, as in PackLaunch
+    int32_t n_src;
+    int32_t chunk_shift;
+    int32_t R;
+    int64_t g_lo;                // reduce flat indices [g_lo, g_hi)
+    int64_t g_hi;
+    int64_t base;                // flat index of shard[0] (rank * S)
+    uint16_t* shard;             // device, 2-byte aligned
+};
+
+hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
 // shard step kernels
 // ---------------------------------------------------------------------------
 

@@ -233,20 +233,21 @@ def special_positions(w: ShardWorkload, n: int = None) -> Tuple[np.ndarray, np.n
     return pos.astype(np.int64), vals
 
 
-def pack_sources(w: PackWorkload, device=None, views: bool = False):
+def pack_sources(w: PackWorkload, device=None, views: bool = False, draw: int = 0):
     """The fp16 gradient tensors of the pack workload, N(0, 1e-3), as a list
     of torch.int16 tensors on `device`.  Drawn in one flat array (host array
     when small) and split into separately allocated tensors, or, with
     views=True, as views of one freshly drawn buffer with a 1..7-element gap
     before each tensor (same distribution and alignment mix, and no
-    per-tensor copy at all)."""
+    per-tensor copy at all).  `draw` selects an independent set of values
+    with the same shapes (another rank's gradients for the reduce)."""
     import torch
     out = []
     total = w.psi
     if views:
         gaps = host_rng(w.wid, KIND_PACK, 1, 0).integers(1, 8, size=len(w.numels))
         n_buf = total + int(gaps.sum()) + 8
-        buf = normal_f32(n_buf, 1e-3, w.wid, KIND_PACK, 2, 0, device).to(torch.float16)
+        buf = normal_f32(n_buf, 1e-3, w.wid, KIND_PACK, 2, draw, device).to(torch.float16)
         off = 0
         for n, gap in zip(w.numels, gaps):
             off += int(gap)
@@ -254,11 +255,11 @@ def pack_sources(w: PackWorkload, device=None, views: bool = False):
             off += n
         return out
     if total <= HOST_RNG_LIMIT:
-        flat = normal_f32(total, 1e-3, w.wid, KIND_PACK, 0, 0).to(torch.float16)
+        flat = normal_f32(total, 1e-3, w.wid, KIND_PACK, 0, draw).to(torch.float16)
         if device is not None:
             flat = flat.to(device)
     else:
-        flat = normal_f32(total, 1e-3, w.wid, KIND_PACK, 0, 0, device).to(torch.float16)
+        flat = normal_f32(total, 1e-3, w.wid, KIND_PACK, 0, draw, device).to(torch.float16)
     off = 0
     for n in w.numels:
         out.append(flat[off:off + n].clone().view(torch.int16))

@@ -1,0 +1,123 @@
+"""GPU parity of the bucket reduce-to-owner (through the C ABI) against the
+oracle: every fill and every owner of small ragged layouts with misaligned
+sources and shard bases and R = 1..7 contributions (bit-exact, untouched
+elements unchanged), and the 20,000-tensor stream with R = 2 over all 82
+fills and 16 owners (three whole fills and a million sampled elements
+compared)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_zero_partition_amd as zp
+from oracle import layout as OL
+from sharded_zero_partition_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7BCD
+
+
+def _lists(rng, numels, R):
+    """R lists of device tensors carved from one buffer per rank at random
+    2-byte offsets, with values up to a few hundred (sums stay finite)."""
+    out = []
+    for _ in range(R):
+        gaps = rng.integers(0, 9, size=len(numels))
+        total = int(sum(numels) + gaps.sum() + 8)
+        vals = (rng.standard_normal(total, dtype=np.float32) * 100).astype(np.float16)
+        buf = torch.from_numpy(vals.view(np.int16)).cuda()
+        lst, off = [], 0
+        for n, g in zip(numels, gaps):
+            off += int(g)
+            lst.append(buf[off:off + n])
+            off += n
+        out.append(lst)
+    return out
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 7])
+def test_small_all_fills_and_owners(R):
+    rng = np.random.default_rng(100 + R)
+    for trial in range(4):
+        numels = [int(x) for x in rng.choice([0, 1, 2, 7, 8, 9, 31, 300, 2049, 5000], size=25)]
+        n_ranks = int(rng.integers(1, 6))
+        bucket = int(rng.choice([1, 13, 64, 1000, 4099]))
+        align = int(rng.choice([1, 8]))
+        lay = zp.partition_layout(numels, n_ranks, stage=2, align=align, bucket=bucket)
+        olay = OL.partition_layout(numels, n_ranks, 2, align, bucket)
+        lists = _lists(rng, numels, R)
+        lay.bind_contributions(lists)
+        host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+        S = olay.shard
+        for r in range(n_ranks):
+            mis = int(rng.integers(0, 8))                 # shard base phase
+            holder = torch.full((S + 16,), SENT, dtype=torch.int16, device="cuda")
+            shard = holder[mis:mis + S]
+            want = np.full(S, SENT, np.uint16)
+            for k in range(olay.n_fills):
+                n = lay.reduce_to_owner(k, r, shard)
+                off, vals = oracle.reduce_to_owner(host, olay, k, r)
+                assert n == vals.size
+                want[off:off + vals.size] = vals
+            got = shard.cpu().numpy().view(np.uint16)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                raise AssertionError(f"trial {trial} rank {r}: {bad.size} differ, first {bad[0]}")
+            h = holder.cpu().numpy().view(np.uint16)
+            assert (h[:mis] == SENT).all() and (h[mis + S:] == SENT).all()
+
+
+def test_errors():
+    numels = [10, 20]
+    lay = zp.partition_layout(numels, 2, bucket=16)
+    shard = torch.zeros(lay.info.shard_elems, dtype=torch.int16, device="cuda")
+    with pytest.raises(zp.ZeroError, match="STATE"):
+        lay.reduce_to_owner(0, 0, shard)                  # nothing bound
+    lists = [[torch.zeros(n, dtype=torch.int16, device="cuda") for n in numels] for _ in range(2)]
+    lay.bind_contributions(lists)
+    with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+        lay.reduce_to_owner(2, 0, shard)                  # fills 0 and 1 only
+    with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+        lay.reduce_to_owner(0, 2, shard)                  # ranks 0 and 1 only
+    with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+        lay.bind_contributions([lists[0]] * 17)           # R <= 16
+    with pytest.raises(zp.ZeroError, match="STATE"):
+        zp.partition_layout(numels, 2).bind_contributions(lists)   # no bucket plan
+    # psi = 30, S = 15, B = 16: fill 1 is [16, 30), rank 0 owns [0, 15)
+    assert lay.reduce_to_owner(1, 0, shard) == 0
+    assert lay.reduce_to_owner(0, 1, shard) == 1          # flat index 15 only
+
+
+def test_pack_20k_two_ranks_full_size():
+    w = W.pack_20k()
+    print(f"[reduce pack_20k] psi={w.psi} fills={w.n_fills} owners={w.n_ranks}", flush=True)
+    lists = [W.pack_sources(w, device="cuda", draw=d) for d in range(2)]
+    lay = zp.partition_layout(w.numels, w.n_ranks, stage=2, bucket=w.bucket)
+    olay = OL.partition_layout(w.numels, w.n_ranks, 2, 1, w.bucket, with_segments=False)
+    lay.bind_contributions(lists)
+    S = olay.shard
+    flat = torch.full((w.n_ranks * S,), SENT, dtype=torch.int16, device="cuda")
+    written = 0
+    for k in range(w.n_fills):
+        for r in range(w.n_ranks):
+            written += lay.reduce_to_owner(k, r, flat[r * S:(r + 1) * S])
+    torch.cuda.synchronize()
+    assert written == w.psi
+    got = flat.cpu().numpy().view(np.uint16)
+    assert (got[w.psi:] == SENT).all()                    # padding never written
+    host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+    # three whole fills through the oracle
+    for k in (0, w.n_fills // 2, w.n_fills - 1):
+        for r in range(w.n_ranks):
+            off, vals = oracle.reduce_to_owner(host, olay, k, r)
+            if vals.size:
+                seg = got[r * S + off:r * S + off + vals.size]
+                assert np.array_equal(seg, vals), (k, r)
+    # a million sampled elements across all fills
+    rng = np.random.default_rng(7)
+    idx = np.sort(rng.integers(0, w.psi, size=1_000_000))
+    flats = [np.concatenate(h) for h in host]
+    vals = oracle.float_to_half(oracle.reduce([f[idx] for f in flats]))
+    assert np.array_equal(got[idx], vals)
