@@ -168,3 +168,21 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert b"R must be" in zp.lib.zero_last_error() or True
     # nothing was modified
     assert sc.scale == 1024.0 and st.t == 0
+
+
+def test_reduce_to_owner_argument_errors_need_no_device(zp):
+    """Argument checks of the contribution binding and the reduce run before
+    any HIP call."""
+    lay = zp.partition_layout([10, 20], 2, bucket=16)
+    ptrs = (ctypes.c_void_p * 4)(1 << 32, (1 << 32) + 64, (1 << 32) + 128, (1 << 32) + 192)
+    assert zp.lib.zero_layout_bind_contributions(lay._h, 0, ptrs, None) == -1      # R < 1
+    assert zp.lib.zero_layout_bind_contributions(lay._h, 17, ptrs, None) == -1     # R > 16
+    bad = (ctypes.c_void_p * 4)(1 << 32, (1 << 32) + 65, (1 << 32) + 128, (1 << 32) + 192)
+    assert zp.lib.zero_layout_bind_contributions(lay._h, 2, bad, None) == -2      # odd address
+    nul = (ctypes.c_void_p * 4)(1 << 32, None, (1 << 32) + 128, (1 << 32) + 192)
+    assert zp.lib.zero_layout_bind_contributions(lay._h, 2, nul, None) == -1
+    nob = zp.partition_layout([10, 20], 2)
+    assert zp.lib.zero_layout_bind_contributions(nob._h, 2, ptrs, None) == -7     # no bucket plan
+    n = ctypes.c_int64()
+    assert zp.lib.zero_reduce_to_owner(lay._h, 0, 0, ctypes.c_void_p(1 << 32), None,
+                                       ctypes.byref(n)) == -7                     # not bound
