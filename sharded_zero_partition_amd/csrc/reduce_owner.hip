@@ -16,9 +16,12 @@
 // owns 2 x 64 consecutive vectors (two 1 KiB store groups).  It reads the
 // source range of its span from the chunk index built at bind time; when the
 // span lies inside one tensor the tensor's offset, length and R addresses are
-// wave-uniform (scalar loads).  For each vector whose 8 elements lie in one
-// tensor, each contribution is read as aligned 16-byte blocks (funnel-shifted
-// when misaligned); vectors at the range ends or across tensor boundaries go
+// wave-uniform (scalar loads), and so is each contribution's misalignment
+// phase: every lane then loads one aligned block per vector group and takes
+// the following block from its neighbour lane by cross-lane shuffle.
+// Otherwise, for each vector whose 8 elements lie in one tensor, each
+// contribution is read as aligned 16-byte blocks (funnel-shifted when
+// misaligned); vectors at the range ends or across tensor boundaries go
 // element by element.  HBM bytes per element: 2R read + 2 written.
 #include "vec16.hpp"
 #include "zp_internal.hpp"
@@ -85,6 +88,71 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
     if (one) {
         one_off = a.off[lo];
         one_len = a.len[lo];
+    }
+
+    // Cooperative path: a span of full vectors inside one tensor has one
+    // misalignment phase per contribution for the whole wave, so each lane
+    // loads one aligned block per vector group and takes the block after it
+    // from the next lane (the last lane from the next group's first lane, or
+    // from one extra block after the span).
+    const bool full_span = kw * 8 - mis >= j_lo && (kw + kSpanVec) * 8 - mis <= j_hi;
+    if (one && full_span) {
+        const int64_t rel0 = a.base + kw * 8 - mis - one_off;    // >= 0, span inside the tensor
+        bool in_bounds = true;
+        for (int r = 0; r < nr; ++r) {
+            const uint16_t* t = a.ptr[int64_t(r) * a.n_src + lo];
+            const uint16_t* p0 = t + rel0;
+            const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+            const uint16_t* b0 = p0 - ph;
+            const int64_t need = ph ? 8 * kSpanVec + 8 : 8 * kSpanVec;
+            in_bounds = in_bounds && b0 >= t && b0 + need <= t + one_len;
+        }
+        if (in_bounds) {
+            float s[kU][8];
+            for (int r = 0; r < nr; ++r) {
+                const uint16_t* t = a.ptr[int64_t(r) * a.n_src + lo];
+                const uint16_t* p0 = t + rel0;
+                const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+                const uint16_t* b0 = p0 - ph;
+                u32x4 v[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u)
+                    v[u] = *reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane);
+                u32x4 extra = v[kU - 1];
+                if (ph) extra = *reinterpret_cast<const u32x4*>(b0 + 8 * kSpanVec);
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    u32x4 nxt;
+                    nxt.x = __shfl_down(v[u].x, 1);
+                    nxt.y = __shfl_down(v[u].y, 1);
+                    nxt.z = __shfl_down(v[u].z, 1);
+                    nxt.w = __shfl_down(v[u].w, 1);
+                    const u32x4 head = u + 1 < kU ? v[u + 1 < kU ? u + 1 : u] : extra;
+                    u32x4 first_of_next;
+                    first_of_next.x = __shfl(head.x, 0);
+                    first_of_next.y = __shfl(head.y, 0);
+                    first_of_next.z = __shfl(head.z, 0);
+                    first_of_next.w = __shfl(head.w, 0);
+                    if (lane == 63) nxt = first_of_next;
+                    const u32x4 wv = window8(v[u], nxt, ph);
+                    const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
+                        s[u][e] = r == 0 ? x : s[u][e] + x;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                uint32_t o[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
+                const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
+                *reinterpret_cast<u32x4*>(a.shard + jv) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+            return;
+        }
     }
 
 #pragma unroll
