@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
                 u32x4 v[kU];
 #pragma unroll
                 for (int u = 0; u < kU; ++u)
-                    v[u] = *reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane);
+                    v[u] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane));
                 u32x4 extra = v[kU - 1];
                 if (ph) extra = *reinterpret_cast<const u32x4*>(b0 + 8 * kSpanVec);
 #pragma unroll
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
 #pragma unroll
                 for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
                 const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
-                *reinterpret_cast<u32x4*>(a.shard + jv) = u32x4{o[0], o[1], o[2], o[3]};
+                __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
+                                            reinterpret_cast<u32x4*>(a.shard + jv));
             }
             return;
         }
