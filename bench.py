@@ -275,6 +275,8 @@ def main():
                    "gather_slots": w.gather_slots, "slot_offset_elems": begin},
         "algorithmic_gbs_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9, 1),
         "kernel_ms": round(kern_avg_ms, 4),
+        "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
+        "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
