@@ -14,13 +14,17 @@
 // (dynamic loss scaling; not on the page).
 //
 // Every element is independent and the kernel moves 26 + 2R bytes per element
-// for about 60 ALU operations, so it is bound by HBM bandwidth.  Design:
-//   - grid-stride loop over 8-element vectors: one 128-bit load per fp16
-//     contribution (8 halves), two 128-bit loads per fp32 array, the same
-//     stores; a scalar tail for S mod 8;
+// for about 80 ALU operations, so it is bound by HBM bandwidth.  Design:
+//   - R = 1, 2, 4: a persistent grid (one 256-thread block per CU) whose waves
+//     walk 1024-element tiles with a register double buffer -- the loads of
+//     the next tile are in flight while the current one is computed -- and
+//     fully coalesced 128/64-bit accesses (step_kernel_tiled); other R: a
+//     grid-stride loop over 8-element vectors (step_kernel); a scalar tail
+//     for the elements past the last whole tile or vector;
 //   - the fp32 arithmetic is written in the order of the definition with one
 //     rounding per operation (no contraction, IEEE division and square root),
-//     so the results match a scalar reference bit for bit;
+//     so the results match a scalar reference bit for bit; with the pipelined
+//     schedule this costs no time (the ALU work hides under the HBM traffic);
 //   - the overflow flag is a wave-level ballot followed by one atomic per
 //     wave that saw a non-finite sum; the flag word holds the epoch of the
 //     call that raised it, so it never has to be cleared between calls;
