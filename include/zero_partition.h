@@ -27,7 +27,8 @@
  *     buffer it passes; the library keeps no pointer beyond the call except
  *     the tensor table given to zero_layout_bind_tensors.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     Device work is ordered on that stream.
+ *     Device work is ordered on that stream, which must belong to the
+ *     current device (a stream of another device is a STATE error).
  *   - Flat indices and sizes are int64_t.
  */
 #ifndef ZERO_PARTITION_H

@@ -38,6 +38,16 @@ int fail_hip(hipError_t err, const char* what) {
 
 void clear_error() { g_last_error.clear(); }
 
+int check_stream_device(void* stream, int dev, const char* what) {
+    if (!stream) return ZERO_OK;
+    hipDevice_t sdev = -1;
+    const hipError_t e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamGetDevice");
+    if (int(sdev) != dev)
+        return fail(ZERO_ERR_STATE, std::string(what) + ": the stream belongs to another device");
+    return ZERO_OK;
+}
+
 namespace {
 
 int env_int(const char* name, int dflt, int lo, int hi) {
@@ -236,8 +246,10 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+        int rc = zp::check_stream_device(stream, dev, "zero_shard_step");
+        if (rc != ZERO_OK) return rc;
         zp::DeviceWorkspace* ws = nullptr;
-        int rc = zp::get_workspace(dev, &ws);
+        rc = zp::get_workspace(dev, &ws);
         if (rc != ZERO_OK) return rc;
         std::lock_guard<std::mutex> lock(ws->mu);
         hipStream_t s = static_cast<hipStream_t>(stream);

@@ -420,6 +420,8 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
     if (dev != l->device) return zp::fail(ZERO_ERR_STATE, "layout was bound on another device");
+    const int src = zp::check_stream_device(stream, dev, "zero_pack_bucket");
+    if (src != ZERO_OK) return src;
 
     zp::PackLaunch a;
     a.src = l->d_src;
@@ -532,6 +534,8 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
     if (dev != l->r_device) return zp::fail(ZERO_ERR_STATE, "contributions were bound on another device");
+    const int src = zp::check_stream_device(stream, dev, "zero_reduce_to_owner");
+    if (src != ZERO_OK) return src;
 
     // [fill*B, (fill+1)*B) meets [rank*S, (rank+1)*S) and [0, psi)
     const int64_t fill_lo = fill * l->bucket;                        // < psi

@@ -112,6 +112,10 @@ hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t
 // a skipped ping-pong step): out16[i] = fp16(p_in[i]).
 hipError_t launch_slot_from_master(const StepLaunch& a, int cu_count, hipStream_t stream);
 
+// ZERO_OK when `stream` (NULL = the null stream) belongs to device `dev`,
+// else a STATE error naming `what`.
+int check_stream_device(void* stream, int dev, const char* what);
+
 // Kernel timing (zero_set_kernel_timing): begin/end mark the first and last
 // kernel of a call on its stream; both are no-ops while timing is disabled.
 hipError_t timing_begin(hipStream_t stream);
