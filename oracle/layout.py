@@ -207,3 +207,60 @@ def owner_range(lay: Layout, fill: int, rank: int):
     lo = max(fill * lay.bucket, rank * lay.shard)
     hi = min((fill + 1) * lay.bucket, (rank + 1) * lay.shard, lay.psi)
     return lo, hi
+
+
+# ---------------------------------------------------------------------------
+# contiguous arena (memory defragmentation paragraph, ZeRO-R)
+# ---------------------------------------------------------------------------
+
+ARENA_KINDS = (["param16", "grad16", "master", "momentum", "variance",
+                "master_alt", "momentum_alt", "variance_alt", "bucket"]
+               + [f"contrib{r}" for r in range(16)])
+ARENA_ORDER = (["master", "momentum", "variance", "master_alt", "momentum_alt", "variance_alt",
+                "grad16"] + [f"contrib{r}" for r in range(16)] + ["param16", "bucket"])
+
+
+def arena_plan(lay: Layout, pingpong: bool = False, n_contrib: int = 0,
+               with_bucket: bool = False, align_bytes: int = 1 << 21):
+    """One rank's buffers laid out in one contiguous block, each starting on
+    an align_bytes boundary.  The model-states paragraph fixes the element
+    sizes (fp16 parameters and gradients, fp32 master/momentum/variance) and
+    the stage paragraphs which of them are 1/N slices:
+
+      param16             S at stage 3, else the padded N*S vector
+      grad16              S at stages 2-3, else N*S
+      master/momentum/
+      variance (+ alt)    S at stages 1-3, else N*S
+      contrib0..R-1       S each (the R fp16 contributions of the shard step)
+      bucket              B (the constant-size buffer)
+
+    Returns {kind: (offset, bytes)} for the kinds present and the total size.
+    Order in the block: fp32 state, alternate state, gradients,
+    contributions, parameters, bucket."""
+    S, P = lay.shard, lay.padded
+    st = lay.stage
+    elems = {
+        "param16": (S if st >= 3 else P, 2),
+        "grad16": (S if st >= 2 else P, 2),
+        "master": (S if st >= 1 else P, 4),
+        "momentum": (S if st >= 1 else P, 4),
+        "variance": (S if st >= 1 else P, 4),
+    }
+    if pingpong:
+        for k in ("master", "momentum", "variance"):
+            elems[k + "_alt"] = elems[k]
+    for r in range(n_contrib):
+        elems[f"contrib{r}"] = (S, 2)
+    if with_bucket:
+        elems["bucket"] = (lay.bucket, 2)
+    plan = {}
+    off = 0
+    for kind in ARENA_ORDER:
+        if kind not in elems:
+            continue
+        n, size = elems[kind]
+        off = -(-off // align_bytes) * align_bytes
+        plan[kind] = (off, n * size)
+        off += n * size
+    return plan, off
+

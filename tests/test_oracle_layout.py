@@ -293,3 +293,40 @@ def test_reduce_to_owner_tiles_the_whole_vector():
     # R = 3 fp32 sums of fp16 values equal the exact sums here (|x| < 8, 11-bit
     # significands, well inside 24 bits), so one rounding to fp16 is the answer
     assert np.array_equal(got[:lay.psi], total.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# contiguous arena
+# ---------------------------------------------------------------------------
+
+def test_arena_bytes_are_the_memory_model():
+    """Without extras and without padding the arena's five model-state kinds
+    add up to the page's per-rank figures: 16 Psi, (4 + 12/N) Psi,
+    (2 + 14/N) Psi and 16 Psi / N."""
+    for n in (1, 4, 64):
+        psi = n * 4099
+        for stage in range(4):
+            lay = OL.partition_layout([psi], n, stage=stage, with_segments=False)
+            plan, total = OL.arena_plan(lay, align_bytes=256)
+            kinds = sum(plan[k][1] for k in ("param16", "grad16", "master", "momentum", "variance"))
+            assert kinds == OL.stage_bytes_per_rank(psi, n, stage)
+            assert kinds == [16 * psi, 4 * psi + 12 * psi // n, 2 * psi + 14 * psi // n,
+                             16 * psi // n][stage]
+
+
+def test_arena_layout_invariants():
+    rng = random.Random(31)
+    for _ in range(200):
+        numels, n_ranks, align, bucket = _random_case(rng)
+        lay = OL.partition_layout(numels, n_ranks, rng.randint(0, 3), align, bucket,
+                                  with_segments=False)
+        ab = rng.choice([256, 4096, 1 << 21])
+        plan, total = OL.arena_plan(lay, pingpong=rng.random() < 0.5, n_contrib=rng.randint(0, 4),
+                                    with_bucket=bucket > 0 and rng.random() < 0.5, align_bytes=ab)
+        spans = sorted(plan.values())
+        for (o, b) in spans:
+            assert o % ab == 0 and b >= 0
+        for (o1, b1), (o2, b2) in zip(spans, spans[1:]):
+            assert o1 + b1 <= o2                        # disjoint, in order
+        assert total == spans[-1][0] + spans[-1][1]
+        assert total - sum(b for _, b in spans) < len(spans) * ab   # only alignment gaps
