@@ -74,6 +74,9 @@ def parse_args():
                     help="also run a plain 2 GiB device copy (scale reference for HBM counters)")
     ap.add_argument("--pack-views", action="store_true",
                     help="pack sources as views of one buffer instead of 20,000 allocations")
+    ap.add_argument("--arena", action="store_true",
+                    help="carve the shard state, its alternate set and the contributions out of "
+                         "one contiguous block (zero_arena_plan_for) instead of separate allocations")
     return ap.parse_args()
 
 
@@ -112,12 +115,29 @@ def main():
     slot = gather[w.rank * S:(w.rank + 1) * S]
     p0 = W.master_init(w, device=dev)
     slot.copy_(p0.to(torch.float16).view(torch.int16))
-    if args.mode == "pingpong":
+    arena = None
+    if args.arena:
+        alay = zp.partition_layout(w.numels, w.n_ranks, stage=w.stage)
+        arena = zp.carve_arena(alay.arena_plan(pingpong=args.mode == "pingpong", n_contrib=R))
+        alay.close()
+        arena["master"].copy_(p0)
+        arena["momentum"].zero_()
+        arena["variance"].zero_()
+        del p0
+        p0 = arena["master"]
+        alt = [arena.get(k) for k in ("master_alt", "momentum_alt", "variance_alt")]
+        st = zp.ShardState(p0, arena["momentum"], arena["variance"], *alt)
+        grads = []
+        for r in range(R):
+            arena[f"contrib{r}"].copy_(W.grad_contribution(w, 1, r, w.scale, device=dev))
+            grads.append(arena[f"contrib{r}"])
+    elif args.mode == "pingpong":
         st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0),
                            torch.empty_like(p0), torch.empty_like(p0), torch.empty_like(p0))
+        grads = [W.grad_contribution(w, 1, r, w.scale, device=dev) for r in range(R)]
     else:
         st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0))
-    grads = [W.grad_contribution(w, 1, r, w.scale, device=dev) for r in range(R)]
+        grads = [W.grad_contribution(w, 1, r, w.scale, device=dev) for r in range(R)]
     hp = zp.AdamHParams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
     scaler = zp.LossScaler.make(w.scale)
 
@@ -156,7 +176,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
-    del st, grads, gather, slot, p0
+    del st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
 
     if args.calibration_copy:
@@ -272,6 +292,7 @@ def main():
         "config": {"workload": "zero3_13b: rank 63 of 64, 13B-param GPT-style model "
                                "(40 layers, hidden 5120, FFN 20480, vocab 50257)",
                    "shard_elems": S, "contributions": R, "mode": args.mode,
+                   "state_allocation": "one contiguous arena" if args.arena else "separate buffers",
                    "gather_slots": w.gather_slots, "slot_offset_elems": begin},
         "algorithmic_gbs_per_step": round(alg_bytes / (step_ms * 1e-3) / 1e9, 1),
         "kernel_ms": round(kern_avg_ms, 4),

@@ -141,6 +141,47 @@ int zero_layout_fill_segments(const zero_layout* layout, int64_t fill, zero_segm
                               int64_t cap, int64_t* n_out);
 
 /* ------------------------------------------------------------------------ */
+/* Contiguous arena for one rank's buffers (memory defragmentation paragraph)*/
+/* ------------------------------------------------------------------------ */
+
+/* Buffer kinds of one rank, in the order of zero_arena_plan.offset/bytes. */
+enum {
+    ZERO_ARENA_PARAM16 = 0,      /* fp16 parameters: S at stage 3, else N*S    */
+    ZERO_ARENA_GRAD16 = 1,       /* fp16 gradients: S at stages 2-3, else N*S  */
+    ZERO_ARENA_MASTER = 2,       /* fp32 master: S at stages 1-3, else N*S     */
+    ZERO_ARENA_MOMENTUM = 3,     /* fp32 momentum, as master                   */
+    ZERO_ARENA_VARIANCE = 4,     /* fp32 variance, as master                   */
+    ZERO_ARENA_MASTER_ALT = 5,   /* ping-pong alternates, as master            */
+    ZERO_ARENA_MOMENTUM_ALT = 6,
+    ZERO_ARENA_VARIANCE_ALT = 7,
+    ZERO_ARENA_BUCKET = 8,       /* fp16 constant-size bucket: B               */
+    ZERO_ARENA_CONTRIB0 = 9,     /* fp16 contribution r at CONTRIB0 + r: S     */
+    ZERO_ARENA_KINDS = 25
+};
+
+typedef struct zero_arena_plan {
+    int64_t total_bytes;                 /* size of the one allocation        */
+    int64_t align_bytes;                 /* every buffer starts on a multiple */
+    int64_t offset[ZERO_ARENA_KINDS];    /* byte offset, -1 when absent        */
+    int64_t bytes[ZERO_ARENA_KINDS];     /* byte size, 0 when absent           */
+} zero_arena_plan;
+
+/* Lay out one rank's buffers in a single contiguous block (host only; the
+ * caller allocates total_bytes once and carves the buffers).  Element sizes
+ * follow the model-states paragraph and the partitioned kinds the stage
+ * paragraphs, so the five model-state kinds add up to the page's per-rank
+ * bytes (plus padding).  Order: fp32 state, alternates, fp16 gradients,
+ * contributions, fp16 parameters, bucket.
+ *   pingpong     1: also the alternate master/momentum/variance set
+ *   n_contrib    0..16 fp16 contribution buffers of S elements
+ *   with_bucket  1: one bucket of B elements (the layout needs a bucket plan)
+ *   align_bytes  power of two >= 256 (0: 2 MiB)
+ * Errors: INVALID_ARG, STATE (bucket requested without a bucket plan),
+ * INDEX_OVERFLOW. */
+int zero_arena_plan_for(const zero_layout* layout, int32_t pingpong, int32_t n_contrib,
+                        int32_t with_bucket, int64_t align_bytes, zero_arena_plan* out);
+
+/* ------------------------------------------------------------------------ */
 /* Bucket pack (constant-size buffers paragraph)                             */
 /* ------------------------------------------------------------------------ */
 
@@ -292,7 +333,7 @@ const char* zero_last_error(void);     /* thread-local, never NULL */
 int zero_last_hip_error(void);         /* hipError_t of the last ZERO_ERR_HIP */
 
 /* sizeof of the ABI structs, for binding checks: 0 layout_info, 1 segment,
- * 2 shard_state, 3 adam_hparams, 4 loss_scaler; -1 otherwise. */
+ * 2 shard_state, 3 adam_hparams, 4 loss_scaler, 5 arena_plan; -1 otherwise. */
 int64_t zero_abi_struct_size(int32_t which);
 
 /* Architecture of the current device as a number (gfx950 -> 950) and its

@@ -83,7 +83,20 @@ class LossScaler(ctypes.Structure):
         return cls(scale, backoff, growth, min_scale, growth_interval, good_steps)
 
 
-ABI_STRUCTS = [LayoutInfo, Segment, ShardStateC, AdamHParams, LossScaler]
+ARENA_KINDS = (["param16", "grad16", "master", "momentum", "variance", "master_alt",
+                "momentum_alt", "variance_alt", "bucket"] + [f"contrib{r}" for r in range(16)])
+
+
+class ArenaPlan(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_int64), ("align_bytes", ctypes.c_int64),
+                ("offset", ctypes.c_int64 * 25), ("bytes", ctypes.c_int64 * 25)]
+
+    def as_dict(self):
+        return {k: (self.offset[i], self.bytes[i]) for i, k in enumerate(ARENA_KINDS)
+                if self.offset[i] >= 0}
+
+
+ABI_STRUCTS = [LayoutInfo, Segment, ShardStateC, AdamHParams, LossScaler, ArenaPlan]
 
 # exported symbol -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -97,6 +110,7 @@ SIGNATURES = {
     "zero_layout_segments": (ctypes.c_int, [_P, _P, _I64, _P]),
     "zero_layout_rank_segments": (ctypes.c_int, [_P, _I32, _P, _I64, _P]),
     "zero_layout_fill_segments": (ctypes.c_int, [_P, _I64, _P, _I64, _P]),
+    "zero_arena_plan_for": (ctypes.c_int, [_P, _I32, _I32, _I32, _I64, _P]),
     "zero_layout_bind_tensors": (ctypes.c_int, [_P, _P, _P]),
     "zero_pack_bucket": (ctypes.c_int, [_P, _I64, _P, _P, _P]),
     "zero_layout_bind_contributions": (ctypes.c_int, [_P, _I32, _P, _P]),
@@ -219,6 +233,14 @@ class Layout:
 
     def fill_segments(self, fill: int) -> List[Segment]:
         return self._query(lib.zero_layout_fill_segments, int(fill))
+
+    def arena_plan(self, pingpong: bool = False, n_contrib: int = 0, with_bucket: bool = False,
+                   align_bytes: int = 0) -> ArenaPlan:
+        """zero_arena_plan_for: one rank's buffers in one contiguous block."""
+        out = ArenaPlan()
+        _check(lib.zero_arena_plan_for(self._h, int(bool(pingpong)), int(n_contrib),
+                                       int(bool(with_bucket)), int(align_bytes), _ref(out)))
+        return out
 
     def bind_tensors(self, tensors, stream=None):
         """Bind the device fp16 tensors (any 2-byte dtype, contiguous) in
@@ -360,3 +382,17 @@ def last_kernel_ms() -> float:
     ms = ctypes.c_float()
     _check(lib.zero_last_kernel_ms(_ref(ms)))
     return ms.value
+
+
+def carve_arena(plan: ArenaPlan, device="cuda"):
+    """Allocate plan.total_bytes once and return {kind: tensor view} (fp32
+    kinds as float32, fp16 kinds as int16 bit patterns)."""
+    import torch
+    arena = torch.empty(plan.total_bytes, dtype=torch.uint8, device=device)
+    views = {"_arena": arena}
+    for kind, (off, nbytes) in plan.as_dict().items():
+        dt = torch.float32 if kind in ("master", "momentum", "variance", "master_alt",
+                                       "momentum_alt", "variance_alt") else torch.int16
+        views[kind] = arena[off:off + nbytes].view(dt)
+    return views
+

@@ -365,6 +365,7 @@ extern "C" int64_t zero_abi_struct_size(int32_t which) {
         case 2: return int64_t(sizeof(zero_shard_state));
         case 3: return int64_t(sizeof(zero_adam_hparams));
         case 4: return int64_t(sizeof(zero_loss_scaler));
+        case 5: return int64_t(sizeof(zero_arena_plan));
         default: return -1;
     }
 }

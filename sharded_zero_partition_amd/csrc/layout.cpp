@@ -568,3 +568,69 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");
     return ZERO_OK;
 }
+
+// ---------------------------------------------------------------------------
+// contiguous arena plan
+// ---------------------------------------------------------------------------
+
+extern "C" int zero_arena_plan_for(const zero_layout* l, int32_t pingpong, int32_t n_contrib,
+                                   int32_t with_bucket, int64_t align_bytes, zero_arena_plan* out) {
+    zp::clear_error();
+    if (!l || !out) return zp::fail(ZERO_ERR_INVALID_ARG, "zero_arena_plan_for: NULL argument");
+    if (n_contrib < 0 || n_contrib > 16) return zp::fail(ZERO_ERR_INVALID_ARG, "n_contrib must be 0..16");
+    if (align_bytes == 0) align_bytes = int64_t(1) << 21;
+    if (align_bytes < 256 || (align_bytes & (align_bytes - 1)))
+        return zp::fail(ZERO_ERR_INVALID_ARG, "align_bytes must be a power of two >= 256");
+    if (with_bucket && l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+
+    const int64_t S = l->shard;
+    const int64_t P = int64_t(l->n_ranks) * S;
+    const int st = l->stage;
+    int64_t elems[ZERO_ARENA_KINDS] = {0};
+    int64_t width[ZERO_ARENA_KINDS] = {0};
+    bool present[ZERO_ARENA_KINDS] = {false};
+    auto want = [&](int kind, int64_t n, int64_t w) {
+        elems[kind] = n;
+        width[kind] = w;
+        present[kind] = true;
+    };
+    want(ZERO_ARENA_PARAM16, st >= 3 ? S : P, 2);
+    want(ZERO_ARENA_GRAD16, st >= 2 ? S : P, 2);
+    for (int k = ZERO_ARENA_MASTER; k <= ZERO_ARENA_VARIANCE; ++k) want(k, st >= 1 ? S : P, 4);
+    if (pingpong)
+        for (int k = ZERO_ARENA_MASTER_ALT; k <= ZERO_ARENA_VARIANCE_ALT; ++k) want(k, st >= 1 ? S : P, 4);
+    for (int r = 0; r < n_contrib; ++r) want(ZERO_ARENA_CONTRIB0 + r, S, 2);
+    if (with_bucket) want(ZERO_ARENA_BUCKET, l->bucket, 2);
+
+    // fp32 state first, then alternates, gradients, contributions, parameters, bucket
+    int order[ZERO_ARENA_KINDS];
+    int n_order = 0;
+    for (int k = ZERO_ARENA_MASTER; k <= ZERO_ARENA_VARIANCE_ALT; ++k) order[n_order++] = k;
+    order[n_order++] = ZERO_ARENA_GRAD16;
+    for (int r = 0; r < 16; ++r) order[n_order++] = ZERO_ARENA_CONTRIB0 + r;
+    order[n_order++] = ZERO_ARENA_PARAM16;
+    order[n_order++] = ZERO_ARENA_BUCKET;
+
+    zero_arena_plan plan;
+    plan.align_bytes = align_bytes;
+    for (int k = 0; k < ZERO_ARENA_KINDS; ++k) {
+        plan.offset[k] = -1;
+        plan.bytes[k] = 0;
+    }
+    constexpr int64_t kMax = std::numeric_limits<int64_t>::max();
+    int64_t off = 0;
+    for (int j = 0; j < n_order; ++j) {
+        const int k = order[j];
+        if (!present[k]) continue;
+        if (off > kMax - (align_bytes - 1)) return zp::fail(ZERO_ERR_INDEX_OVERFLOW, "arena size overflows int64");
+        off = (off + align_bytes - 1) & ~(align_bytes - 1);
+        if (elems[k] > (kMax - off) / width[k]) return zp::fail(ZERO_ERR_INDEX_OVERFLOW, "arena size overflows int64");
+        plan.offset[k] = off;
+        plan.bytes[k] = elems[k] * width[k];
+        off += plan.bytes[k];
+    }
+    plan.total_bytes = off;
+    *out = plan;
+    return ZERO_OK;
+}
+

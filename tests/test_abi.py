@@ -186,3 +186,31 @@ def test_reduce_to_owner_argument_errors_need_no_device(zp):
     n = ctypes.c_int64()
     assert zp.lib.zero_reduce_to_owner(lay._h, 0, 0, ctypes.c_void_p(1 << 32), None,
                                        ctypes.byref(n)) == -7                     # not bound
+
+
+def test_arena_plan_matches_oracle(zp):
+    rng = random.Random(41)
+    for _ in range(200):
+        n_t = rng.randint(0, 10)
+        numels = [rng.choice([0, 1, 5, 100, 4096, 10 ** 6]) for _ in range(n_t)]
+        n_ranks, stage = rng.randint(1, 64), rng.randint(0, 3)
+        align, bucket = rng.choice([1, 8, 64]), rng.choice([0, 1 << 16])
+        pp, nc = rng.random() < 0.5, rng.randint(0, 4)
+        wb = bucket > 0 and rng.random() < 0.5
+        ab = rng.choice([256, 4096, 1 << 21])
+        lay = zp.partition_layout(numels, n_ranks, stage, align, bucket)
+        got = lay.arena_plan(pp, nc, wb, ab)
+        want, total = OL.arena_plan(OL.partition_layout(numels, n_ranks, stage, align, bucket,
+                                                        with_segments=False), pp, nc, wb, ab)
+        assert got.total_bytes == total and got.align_bytes == ab
+        assert got.as_dict() == want
+
+
+def test_arena_plan_errors(zp):
+    lay = zp.partition_layout([100], 4)
+    with pytest.raises(zp.ZeroError, match="STATE"):
+        lay.arena_plan(with_bucket=True)
+    for bad in (dict(n_contrib=17), dict(align_bytes=100), dict(align_bytes=768)):
+        with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
+            lay.arena_plan(**bad)
+    assert lay.arena_plan().align_bytes == 1 << 21
