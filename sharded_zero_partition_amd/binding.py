@@ -162,9 +162,20 @@ def _stream_ptr(stream) -> Optional[int]:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev_ptr(t, what: str, dtype_bytes: int):
+def _current_device() -> int:
+    import torch
+    return torch.cuda.current_device()
+
+
+def _dev_ptr(t, what: str, dtype_bytes: int, dev: int = None):
+    """Device address of a contiguous tensor on the current device (`dev`,
+    when the caller already knows it)."""
     if not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
+    if dev is None:
+        dev = _current_device()
+    if t.device.index != dev:
+        raise ValueError(f"{what} is on {t.device}, the current device is cuda:{dev}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     if t.element_size() != dtype_bytes:
@@ -323,7 +334,7 @@ class ShardState:
             return self.p, self.m, self.v
         return self.p_alt, self.m_alt, self.v_alt
 
-    def _to_c(self) -> ShardStateC:
+    def _to_c(self, dev: int) -> ShardStateC:
         c = ShardStateC()
         c.shard_elems = self.shard_elems
         sets = [(self.p, self.m, self.v)]
@@ -333,7 +344,7 @@ class ShardState:
             for name, t in (("p", p), ("m", m), ("v", v)):
                 if t.numel() != self.shard_elems:
                     raise ValueError(f"{name}[{k}] has {t.numel()} elements, expected {self.shard_elems}")
-                getattr(c, name)[k] = _dev_ptr(t, f"{name}[{k}]", 4) if t.numel() else None
+                getattr(c, name)[k] = _dev_ptr(t, f"{name}[{k}]", 4, dev) if t.numel() else None
         c.cur = self.cur
         c.t = self.t
         return c
@@ -345,16 +356,17 @@ def shard_step(state: ShardState, grads, hparams: AdamHParams, scaler: LossScale
     and the scaler in place."""
     R = len(grads)
     S = state.shard_elems
+    dev = _current_device()
     ptrs = (ctypes.c_void_p * max(1, R))()
     for r, g in enumerate(grads):
         if g.numel() != S:
             raise ValueError(f"grads[{r}] has {g.numel()} elements, expected {S}")
-        ptrs[r] = _dev_ptr(g, f"grads[{r}]", 2) if S else None
+        ptrs[r] = _dev_ptr(g, f"grads[{r}]", 2, dev) if S else None
     if out_slot.numel() != S:
         raise ValueError(f"out_slot has {out_slot.numel()} elements, expected {S}")
-    c = state._to_c()
+    c = state._to_c(dev)
     flag = ctypes.c_int32()
-    slot = ctypes.c_void_p(_dev_ptr(out_slot, "out_slot", 2) if S else None)
+    slot = ctypes.c_void_p(_dev_ptr(out_slot, "out_slot", 2, dev) if S else None)
     _check(lib.zero_shard_step(_ref(c), ptrs, R, _ref(hparams), _ref(scaler), slot,
                                _stream_ptr(stream), _ref(flag)))
     state.t = c.t
