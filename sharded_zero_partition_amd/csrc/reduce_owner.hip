@@ -62,6 +62,65 @@ __device__ __forceinline__ float sum1(const ReduceLaunch& a, int i, int64_t rel)
     return s;
 }
 
+// The next lane's block of each vector group: lane l < 63 takes lane l+1's
+// block of group u, lane 63 the first block of group u+1 (or `extra`).
+__device__ __forceinline__ u32x4 next_block(const u32x4 v[kU], int u, u32x4 extra, int lane) {
+    u32x4 nxt;
+    nxt.x = __shfl_down(v[u].x, 1);
+    nxt.y = __shfl_down(v[u].y, 1);
+    nxt.z = __shfl_down(v[u].z, 1);
+    nxt.w = __shfl_down(v[u].w, 1);
+    const u32x4 head = u + 1 < kU ? v[u + 1 < kU ? u + 1 : u] : extra;
+    u32x4 first_of_next;
+    first_of_next.x = __shfl(head.x, 0);
+    first_of_next.y = __shfl(head.y, 0);
+    first_of_next.z = __shfl(head.z, 0);
+    first_of_next.w = __shfl(head.w, 0);
+    return lane == 63 ? first_of_next : nxt;
+}
+
+// Cooperative span with a compile-time contribution count R: all R * kU
+// aligned blocks (plus the extra blocks) are loaded before any is used.
+template <int R>
+__device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_t rel0, int64_t len,
+                                          int64_t kw, int mis, int lane) {
+    u32x4 v[R][kU];
+    u32x4 extra[R];
+    int ph[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint16_t* t = a.ptr[int64_t(r) * a.n_src + src];
+        const uint16_t* p0 = t + rel0;
+        ph[r] = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+        const uint16_t* b0 = p0 - ph[r];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            v[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane));
+        // aligned: re-read the last group's block rather than past the span
+        extra[r] = *reinterpret_cast<const u32x4*>(b0 + (ph[r] ? 8 * kSpanVec : 512 * (kU - 1) + 8 * lane));
+    }
+    (void)len;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        float s[8];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 wv = window8(v[r][u], next_block(v[r], u, extra[r], lane), ph[r]);
+            const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
+                s[e] = r == 0 ? x : s[e] + x;
+            }
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = f2h(s[2 * d]) | (f2h(s[2 * d + 1]) << 16);
+        const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
+        __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(a.shard + jv));
+    }
+}
+
 template <int R>
 __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaunch a) {
     const int nr = R == 0 ? a.R : R;   // contributions; compile-time unless R == 0
@@ -108,6 +167,12 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
             in_bounds = in_bounds && b0 >= t && b0 + need <= t + one_len;
         }
         if (in_bounds) {
+            if (R > 0) {
+                // compile-time count: every contribution's loads are issued
+                // before the first shuffle
+                coop_span<R == 0 ? 1 : R>(a, lo, rel0, one_len, kw, mis, lane);
+                return;
+            }
             float s[kU][8];
             for (int r = 0; r < nr; ++r) {
                 const uint16_t* t = a.ptr[int64_t(r) * a.n_src + lo];
