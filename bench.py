@@ -84,9 +84,9 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one rank's shard step on a single GPU; runs on more than "
-              "one GPU are not part of this build (the multi-GPU exchange is described in the "
-              "design notes)", file=sys.stderr)
+        print("bench.py measures one rank's shard step on a single GPU; the library has no "
+              "multi-GPU exchange, so --gpus above 1 (or a multi-process launch) is not supported",
+              file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
@@ -142,7 +142,7 @@ def main():
     scaler = zp.LossScaler.make(w.scale)
 
     # host copy of the sample the CPU oracle will take (before any update)
-    cpu_n = min(S, 1 << 27)
+    cpu_n = S                    # the whole shard, one step (~10 s on one core)
     cpu_inputs = None
     if not args.no_cpu_baseline:
         cpu_inputs = (p0[:cpu_n].cpu().numpy().copy(),
@@ -273,7 +273,7 @@ def main():
         cpu_s = time.perf_counter() - t0
         cpu = {"value": round(cpu_n / cpu_s, 1), "unit": "elements/s", "cores": 1,
                "kind": "oracle",
-               "sample": f"first {cpu_n} elements of the rank-63 shard, one step "
+               "sample": f"the whole rank-63 shard ({cpu_n} elements), first step "
                          f"(scalar C oracle, one thread, {cpu_s:.1f} s)"}
 
     out = {

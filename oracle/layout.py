@@ -19,7 +19,7 @@ Trillion Parameter Models", azimuth.plus):
   * constant-size buffers paragraph (ZeRO-R): many small tensors are fused into one
     fixed-size buffer whose size does not depend on the model size.
 
-Readings where the page is silent (each also listed in the design notes):
+Readings where the page is silent:
   * the model states are flattened in tensor-list order with no per-tensor
     padding; the flat vector is cut into N equal shards of S elements, S the
     smallest multiple of the alignment A with N*S >= Psi; rank r owns
