@@ -28,23 +28,6 @@ namespace {
 
 constexpr int kPackThreads = 256;
 
-// Index of the source tensor holding flat index g (g < psi).
-__device__ __forceinline__ int find_src(const PackSrc* __restrict__ src,
-                                        const int32_t* __restrict__ first, int shift,
-                                        int64_t g) {
-    const int64_t c = g >> shift;
-    int lo = first[c];
-    int hi = first[c + 1];
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (src[mid].flat_off <= g)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
 // Element-by-element gather of up to nvalid elements from flat index g on,
 // starting the source walk at index i; zeros past psi.
 __device__ __forceinline__ u32x4 gather8(const PackSrc* __restrict__ src, int i, int64_t g,
@@ -75,14 +58,13 @@ __device__ __forceinline__ int find_src_in(const PackSrc* __restrict__ src, int 
     return lo;
 }
 
-// Wave-span variant.  Wave w owns bucket elements [w*span, (w+1)*span),
-// span = 512 * U; lane l handles the U vectors at offsets 512 u + 8 l, so
-// each of the U store instructions covers 1 KiB of the bucket contiguously.
-// The wave first resolves the source range of its whole span (the same
-// search on every lane, so it is served by the cache), then every lane
-// finds its own source inside that range -- usually a single candidate --
-// and issues the loads of all U vectors before any of them is used, so a
-// lane keeps up to 2U independent 16-byte loads in flight.
+// Wave w owns bucket elements [w*span, (w+1)*span), span = 512 * U; lane l
+// handles the U vectors at offsets 512 u + 8 l, so each of the U store
+// instructions covers 1 KiB of the bucket contiguously.  The wave reads the
+// source range of its span from the chunk index (two scalar loads); a span
+// inside one tensor takes the cooperative path below, otherwise every lane
+// finds its own source inside that range and issues the loads of all U
+// vectors before any of them is used (up to 2U 16-byte loads in flight).
 template <int U>
 __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunch a) {
     constexpr int64_t kSpan = 512 * U;

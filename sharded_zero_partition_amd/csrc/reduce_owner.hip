@@ -33,14 +33,6 @@ constexpr int kThreads = 256;
 constexpr int kU = 2;                     // vectors per lane
 constexpr int64_t kSpanVec = 64 * kU;     // vectors per wave
 
-__device__ __forceinline__ float h2f(uint32_t bits) {
-    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
-}
-
-__device__ __forceinline__ uint32_t f2h(float x) {
-    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(x)));
-}
-
 // Last index i in [lo, hi] with off[i] <= g.
 __device__ __forceinline__ int search(const int64_t* __restrict__ off, int lo, int hi, int64_t g) {
     while (lo < hi) {

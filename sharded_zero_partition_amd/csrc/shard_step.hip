@@ -30,6 +30,7 @@
 //     call that raised it, so it never has to be cleared between calls;
 //   - ping-pong state (read set A, write set B) makes the step a single pass:
 //     the commit is the host flipping the live set once the flag is known.
+#include "vec16.hpp"
 #include "zp_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -38,7 +39,6 @@ namespace zp {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
@@ -48,14 +48,6 @@ constexpr int kOut16B = 0;
 constexpr int kOut8B = 1;
 constexpr int kOut4B = 2;
 constexpr int kOut2B = 3;
-
-__device__ __forceinline__ float h2f(uint32_t bits) {
-    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
-}
-
-__device__ __forceinline__ uint32_t f2h(float x) {
-    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(x)));
-}
 
 __device__ __forceinline__ bool not_finite(float x) {
     return (__builtin_bit_cast(uint32_t, x) & 0x7F800000u) == 0x7F800000u;

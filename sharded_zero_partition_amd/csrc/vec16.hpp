@@ -10,6 +10,17 @@ namespace zp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// fp16 bit pattern -> fp32 (exact) and fp32 -> fp16 bit pattern (round to
+// nearest even, subnormals kept; the hardware conversions under the default
+// rounding and denormal modes).
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+}
+
+__device__ __forceinline__ uint32_t f2h(float x) {
+    return uint32_t(__builtin_bit_cast(uint16_t, _Float16(x)));
+}
+
 __device__ __forceinline__ uint32_t funnel16(uint32_t lo, uint32_t hi) {
     return (lo >> 16) | (hi << 16);
 }
