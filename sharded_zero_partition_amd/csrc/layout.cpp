@@ -370,6 +370,8 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_tensors");
+    if (rc != ZERO_OK) return rc;
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipDeviceGetAttribute");
@@ -488,6 +490,8 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+    const int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_contributions");
+    if (rc != ZERO_OK) return rc;
     const size_t n = std::max<size_t>(1, offs.size());
     void* d[4] = {nullptr, nullptr, nullptr, nullptr};
     const size_t bytes[4] = {n * sizeof(int64_t), n * sizeof(int64_t),
