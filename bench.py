@@ -9,8 +9,8 @@ check, applies Adam to its fp32 master/momentum/variance shard and writes the
 fp16 parameters into its slot of a 64-slot gather buffer (25.7 GB).  All
 inputs are synthetic and resident in HBM before the timed region.
 
-A timed step is one zero_shard_step call (fused kernel, overflow read-back,
-loss-scale control).  The same run also reports
+A timed step is one zero_shard_step call (fused kernel, the overflow decision
+that its last block publishes to the host, loss-scale control).  The same run also reports
   * the partition layout of the 484-tensor model (host, once per model),
   * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
   * the owners' share of the bucketed reduce of two ranks' copies of that
@@ -88,8 +88,8 @@ def main():
               "multi-GPU exchange, so --gpus above 1 (or a multi-process launch) is not supported",
               file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0:
-        sys.exit("--steps must be >= 1 and --warmup >= 0")
+    if args.steps < 1 or args.steps > 4096 or args.warmup < 0:
+        sys.exit("--steps must be in 1..4096 (one kernel-timing pair per step) and --warmup >= 0")
 
     import numpy as np
     import torch
@@ -154,16 +154,16 @@ def main():
 
     # timed region: exactly K steps
     zp.set_kernel_timing(True)
-    kernel_ms = []
     flags = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         flags += zp.shard_step(st, grads, hp, scaler, slot)
-        kernel_ms.append(zp.last_kernel_ms())
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    kernel_ms = zp.kernel_times()          # one event pair per step, read after the loop
     zp.set_kernel_timing(False)
+    assert len(kernel_ms) == args.steps
     assert flags == 0, "unexpected overflow in the benchmark inputs"
 
     step_ms = elapsed / args.steps * 1e3
@@ -201,14 +201,14 @@ def main():
             play.pack_bucket(k, bucket)
         torch.cuda.synchronize()
         zp.set_kernel_timing(True)
-        fill_ms = []
         t0 = time.perf_counter()
         for k in range(pw.n_fills):
             play.pack_bucket(k, bucket)
-            fill_ms.append(zp.last_kernel_ms())
         torch.cuda.synchronize()
         pack_wall = time.perf_counter() - t0
+        fill_ms = zp.kernel_times()
         zp.set_kernel_timing(False)
+        assert len(fill_ms) == pw.n_fills
         kernel_total = float(np.sum(fill_ms)) * 1e-3
         pack_bytes = 4 * pw.psi + 2 * (pw.n_fills * pw.bucket - pw.psi)
         pack_gbs = pack_bytes / kernel_total / 1e9
@@ -236,14 +236,14 @@ def main():
             rlay.reduce_to_owner(k, r, flat[r * S4:(r + 1) * S4])
         torch.cuda.synchronize()
         zp.set_kernel_timing(True)
-        red_ms = []
         t0 = time.perf_counter()
         for k, r in pairs:
             rlay.reduce_to_owner(k, r, flat[r * S4:(r + 1) * S4])
-            red_ms.append(zp.last_kernel_ms())
         torch.cuda.synchronize()
         red_wall = time.perf_counter() - t0
+        red_ms = zp.kernel_times()
         zp.set_kernel_timing(False)
+        assert len(red_ms) == len(pairs)
         red_kernel = float(np.sum(red_ms)) * 1e-3
         red_bytes = 6 * pw.psi                        # 2 x 2 B read + 2 B written
         red_gbs = red_bytes / red_kernel / 1e9

@@ -300,11 +300,16 @@ typedef struct zero_loss_scaler {
  *   out_slot  device, S fp16 values, 2-byte aligned: this rank's slot of the
  *             gather buffer (gather + rank * S)
  *   overflow  host output: 1 if the step was skipped, else 0 (may be NULL)
- * The call blocks until the overflow decision is known (it reads 4 bytes back
- * and waits for `stream`); any work it enqueues after that (restoring the
- * slot of a skipped ping-pong step) is ordered on `stream`.  Calls on one
+ * The call returns once the overflow decision is known: the last block of
+ * the pass writes it into a pinned host word that the call polls, querying
+ * `stream` meanwhile (an error on the stream, or a stream that drains
+ * without the word written, ends the wait with an error).  In ping-pong mode
+ * the pass may still be retiring when the call returns; in place the call
+ * also waits for `stream`.  Everything the call enqueues (the passes, and
+ * restoring the slot of a skipped ping-pong step) is ordered on `stream`:
+ * order later readers of the state or the slot after it.  Calls on one
  * device are serialised by the library.
- * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+ * Errors: INVALID_ARG, ALIGNMENT, STATE, HIP. */
 int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
                     const zero_adam_hparams* hp, zero_loss_scaler* scaler,
                     uint16_t* out_slot, void* stream, int32_t* overflow);
@@ -315,14 +320,21 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
 
 /* Per calling thread.  While enabled (enable != 0), zero_shard_step,
  * zero_pack_bucket and zero_reduce_to_owner record a HIP event before their
- * first and after their last
- * device kernel on the call's stream (for zero_shard_step: the fused pass, or
- * the check and update passes in place; not the flag read-back).
- * zero_last_kernel_ms waits for the last recorded end event and returns the
- * elapsed milliseconds.  Errors: STATE (nothing recorded since enabling),
+ * first and after their last device kernel on the call's stream (for
+ * zero_shard_step: the fused pass, or the check and update passes in place).
+ * The pairs go into a ring of 4096 per thread, so calls can be timed back to
+ * back without waiting on the events; enabling or disabling clears it.
+ * zero_last_kernel_ms waits for the most recent pair's end event and returns
+ * its elapsed milliseconds.  Errors: STATE (nothing recorded since enabling),
  * HIP. */
 int zero_set_kernel_timing(int32_t enable);
 int zero_last_kernel_ms(float* ms);
+
+/* The elapsed milliseconds of every call timed since timing was enabled
+ * (at most the last 4096), oldest first, into ms[0 .. *n); waits for their
+ * events.  *n is always set; ms may be NULL when *n is 0.
+ * Errors: INVALID_ARG (n NULL), CAPACITY (cap < *n), HIP. */
+int zero_kernel_times(float* ms, int64_t cap, int64_t* n);
 
 /* ------------------------------------------------------------------------ */
 /* Misc                                                                      */

@@ -11,7 +11,7 @@ generators; `build` compiles the library.
 
 __all__ = ["partition_layout", "Layout", "ShardState", "shard_step", "AdamHParams",
            "LossScaler", "ZeroError", "version", "device_info", "set_kernel_timing",
-           "last_kernel_ms", "carve_arena", "ArenaPlan"]
+           "last_kernel_ms", "kernel_times", "carve_arena", "ArenaPlan"]
 
 
 def __getattr__(name):

@@ -118,6 +118,7 @@ SIGNATURES = {
     "zero_shard_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
     "zero_set_kernel_timing": (ctypes.c_int, [_I32]),
     "zero_last_kernel_ms": (ctypes.c_int, [_P]),
+    "zero_kernel_times": (ctypes.c_int, [_P, _I64, _P]),
     "zero_version": (ctypes.c_int, []),
     "zero_last_error": (ctypes.c_char_p, []),
     "zero_last_hip_error": (ctypes.c_int, []),
@@ -394,6 +395,15 @@ def last_kernel_ms() -> float:
     ms = ctypes.c_float()
     _check(lib.zero_last_kernel_ms(_ref(ms)))
     return ms.value
+
+
+def kernel_times() -> list:
+    """zero_kernel_times: device time (ms) of every call timed since timing
+    was enabled on this thread (at most the last 4096), oldest first."""
+    n = ctypes.c_int64()
+    buf = (ctypes.c_float * 4096)()
+    _check(lib.zero_kernel_times(buf, 4096, _ref(n)))
+    return [buf[i] for i in range(n.value)]
 
 
 def carve_arena(plan: ArenaPlan, device="cuda"):

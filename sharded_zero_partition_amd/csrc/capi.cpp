@@ -15,6 +15,7 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "zp_internal.hpp"
 
@@ -77,61 +78,83 @@ int blocks_per_cu_pack() {
 
 namespace {
 
-struct ThreadTiming {
-    bool enabled = false;
-    bool recorded = false;
-    int device = -1;
+// Per-thread kernel timing: a ring of HIP event pairs, one pair per timed
+// call, so that calls can be timed back to back and read afterwards.
+constexpr size_t kTimingRing = 4096;
+
+struct EventPair {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;
+    int device = -1;
+};
+
+struct ThreadTiming {
+    bool enabled = false;
+    std::vector<EventPair> ring;   // grows up to kTimingRing entries, then wraps
+    size_t count = 0;              // calls recorded since timing was enabled
+    bool open = false;             // a start event recorded, its stop not yet
+    // the events are not destroyed at thread exit: the HIP runtime may
+    // already be shutting down then
 };
 thread_local ThreadTiming g_timing;
 
-void timing_release() {
-    if (g_timing.start) (void)hipEventDestroy(g_timing.start);
-    if (g_timing.stop) (void)hipEventDestroy(g_timing.stop);
-    g_timing.start = g_timing.stop = nullptr;
-    g_timing.device = -1;
-    g_timing.recorded = false;
-}
+EventPair* current_pair() { return &g_timing.ring[(g_timing.count - 1) % kTimingRing]; }
 
 }  // namespace
 
 hipError_t timing_begin(hipStream_t stream) {
     if (!g_timing.enabled) return hipSuccess;
+    if (g_timing.open) {   // the previous call failed between its two events: reuse its pair
+        g_timing.count -= 1;
+        g_timing.open = false;
+    }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev != g_timing.device) {
-        timing_release();
-        e = hipEventCreate(&g_timing.start);
-        if (e == hipSuccess) e = hipEventCreate(&g_timing.stop);
-        if (e != hipSuccess) {
-            timing_release();
-            return e;
+    const size_t slot = g_timing.count % kTimingRing;
+    if (slot >= g_timing.ring.size()) {
+        try {
+            g_timing.ring.emplace_back();
+        } catch (...) {
+            return hipErrorOutOfMemory;
         }
-        g_timing.device = dev;
     }
-    g_timing.recorded = false;
-    return hipEventRecord(g_timing.start, stream);
+    EventPair& p = g_timing.ring[slot];
+    if (p.device != dev) {
+        if (p.start) (void)hipEventDestroy(p.start);
+        if (p.stop) (void)hipEventDestroy(p.stop);
+        p.start = p.stop = nullptr;
+        p.device = -1;
+        e = hipEventCreate(&p.start);
+        if (e == hipSuccess) e = hipEventCreate(&p.stop);
+        if (e != hipSuccess) return e;
+        p.device = dev;
+    }
+    e = hipEventRecord(p.start, stream);
+    if (e != hipSuccess) return e;
+    g_timing.count += 1;
+    g_timing.open = true;
+    return hipSuccess;
 }
 
 hipError_t timing_end(hipStream_t stream) {
-    if (!g_timing.enabled || !g_timing.start) return hipSuccess;
-    hipError_t e = hipEventRecord(g_timing.stop, stream);
-    if (e == hipSuccess) g_timing.recorded = true;
-    return e;
+    if (!g_timing.enabled || !g_timing.open) return hipSuccess;
+    g_timing.open = false;
+    return hipEventRecord(current_pair()->stop, stream);
 }
 
 namespace {
 
-// Per-device workspace: the overflow flag word and a pinned host word to read
-// it back into.  Created on a device's first shard step and kept until the
-// process ends; `mu` serialises shard steps on the device (they share the
-// flag word).
+// Per-device workspace: the overflow flag word and the blocks-done counter
+// (device, 64 bytes apart) and the pinned, coherent host word that the last
+// block of a pass writes the decision into.  Created on a device's first
+// shard step and kept until the process ends; `mu` serialises shard steps on
+// the device (they share these words).
 struct DeviceWorkspace {
     std::mutex mu;
-    uint32_t* d_flag = nullptr;
-    uint32_t* h_flag = nullptr;
+    uint32_t* d_flag = nullptr;             // d_flag[0] flag; d_flag[16..17] the 64-bit counter
+    unsigned long long* h_word = nullptr;   // host address
+    unsigned long long* h_word_dev = nullptr;   // the same word, device address
     uint32_t epoch = 0;
     int cu_count = 0;
 };
@@ -152,16 +175,49 @@ int get_workspace(int dev, DeviceWorkspace** out) {
         if (e != hipSuccess) return fail_hip(e, "hipMalloc (flag)");
         e = hipMemset(ws->d_flag, 0, 256);
         if (e == hipSuccess)
-            e = hipHostMalloc(reinterpret_cast<void**>(&ws->h_flag), 64, hipHostMallocDefault);
+            e = hipHostMalloc(reinterpret_cast<void**>(&ws->h_word), 64,
+                              hipHostMallocMapped | hipHostMallocCoherent);
+        if (e == hipSuccess) {
+            *ws->h_word = 0;
+            e = hipHostGetDevicePointer(reinterpret_cast<void**>(&ws->h_word_dev), ws->h_word, 0);
+        }
         if (e != hipSuccess) {
+            if (ws->h_word) (void)hipHostFree(ws->h_word);
             (void)hipFree(ws->d_flag);
             return fail_hip(e, "workspace set-up");
         }
-        *ws->h_flag = 0;
         g_ws[dev] = ws.release();
     }
     *out = g_ws[dev];
     return ZERO_OK;
+}
+
+// Waits until the last block of the pass launched with `epoch` has written
+// (epoch << 1) | flag into the host word.  Every 1024 polls the stream is
+// queried: an error there is returned, and a stream that has drained without
+// the word being written is reported rather than waited on.
+int wait_for_flag(DeviceWorkspace* ws, hipStream_t s, uint32_t epoch, int32_t* flag) {
+    const unsigned long long want = epoch;
+    for (unsigned poll = 1;; ++poll) {
+        const unsigned long long w = __atomic_load_n(ws->h_word, __ATOMIC_ACQUIRE);
+        if ((w >> 1) == want) {
+            *flag = int32_t(w & 1ull);
+            return ZERO_OK;
+        }
+        if ((poll & 1023u) == 0) {
+            const hipError_t e = hipStreamQuery(s);
+            if (e == hipSuccess) {
+                const unsigned long long w2 = __atomic_load_n(ws->h_word, __ATOMIC_ACQUIRE);
+                if ((w2 >> 1) == want) {
+                    *flag = int32_t(w2 & 1ull);
+                    return ZERO_OK;
+                }
+                return fail(ZERO_ERR_STATE, "the step's stream drained without the overflow flag being published");
+            }
+            if (e != hipErrorNotReady) return fail_hip(e, "waiting for the shard step");
+        }
+        __builtin_ia32_pause();
+    }
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -254,9 +310,10 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         std::lock_guard<std::mutex> lock(ws->mu);
         hipStream_t s = static_cast<hipStream_t>(stream);
 
-        if (++ws->epoch == 0) {   // the flag word holds epochs; restart after wrap-around
+        if (++ws->epoch == 0) {   // the flag words hold epochs; restart after wrap-around
             e = hipMemsetAsync(ws->d_flag, 0, sizeof(uint32_t), s);
             if (e != hipSuccess) return zp::fail_hip(e, "hipMemsetAsync (flag)");
+            __atomic_store_n(ws->h_word, 0ull, __ATOMIC_RELEASE);
             ws->epoch = 1;
         }
 
@@ -287,6 +344,8 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         a.weight_decay = hp->weight_decay;
         a.flag = ws->d_flag;
         a.epoch = ws->epoch;
+        a.done = reinterpret_cast<unsigned long long*>(ws->d_flag + 16);
+        a.host_word = ws->h_word_dev;
 
         e = zp::timing_begin(s);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
@@ -301,10 +360,14 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         }
         e = zp::timing_end(s);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
-        e = hipMemcpyAsync(ws->h_flag, ws->d_flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return zp::fail_hip(e, "reading the overflow flag");
-        flag = (*ws->h_flag == ws->epoch) ? 1 : 0;
+        rc = zp::wait_for_flag(ws, s, ws->epoch, &flag);
+        if (rc != ZERO_OK) return rc;
+        if (!pingpong) {
+            // the update pass reads the flag word: let it finish before the
+            // next call on this device can raise that word again
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return zp::fail_hip(e, "waiting for the in-place update");
+        }
 
         if (flag && pingpong) {
             // the pass wrote the slot speculatively; restore fp16(master)
@@ -338,17 +401,45 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
 extern "C" int zero_set_kernel_timing(int32_t enable) {
     zp::clear_error();
     zp::g_timing.enabled = enable != 0;
-    zp::g_timing.recorded = false;
+    zp::g_timing.count = 0;
+    zp::g_timing.open = false;
     return ZERO_OK;
 }
+
+namespace zp {
+namespace {
+
+int pair_ms(const EventPair& p, float* ms) {
+    hipError_t e = hipEventSynchronize(p.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, p.start, p.stop);
+    if (e != hipSuccess) return fail_hip(e, "reading kernel timing events");
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zp
 
 extern "C" int zero_last_kernel_ms(float* ms) {
     zp::clear_error();
     if (!ms) return fail(ZERO_ERR_INVALID_ARG, "ms is NULL");
-    if (!zp::g_timing.recorded) return fail(ZERO_ERR_STATE, "no kernel timed since timing was enabled");
-    hipError_t e = hipEventSynchronize(zp::g_timing.stop);
-    if (e == hipSuccess) e = hipEventElapsedTime(ms, zp::g_timing.start, zp::g_timing.stop);
-    if (e != hipSuccess) return zp::fail_hip(e, "reading kernel timing events");
+    const size_t complete = zp::g_timing.count - (zp::g_timing.open ? 1 : 0);
+    if (complete == 0) return fail(ZERO_ERR_STATE, "no kernel timed since timing was enabled");
+    return zp::pair_ms(zp::g_timing.ring[(complete - 1) % zp::kTimingRing], ms);
+}
+
+extern "C" int zero_kernel_times(float* ms, int64_t cap, int64_t* n) {
+    zp::clear_error();
+    if (!n) return fail(ZERO_ERR_INVALID_ARG, "zero_kernel_times: n is NULL");
+    const size_t count = zp::g_timing.count - (zp::g_timing.open ? 1 : 0);
+    const size_t kept = count < zp::kTimingRing ? count : zp::kTimingRing;
+    *n = int64_t(kept);
+    if (kept == 0) return ZERO_OK;
+    if (!ms || cap < int64_t(kept)) return fail(ZERO_ERR_CAPACITY, "timing array too small");
+    for (size_t i = 0; i < kept; ++i) {
+        const size_t call = count - kept + i;   // oldest kept call first
+        const int rc = zp::pair_ms(zp::g_timing.ring[call % zp::kTimingRing], ms + i);
+        if (rc != ZERO_OK) return rc;
+    }
     return ZERO_OK;
 }
 

@@ -25,9 +25,10 @@
 //     rounding per operation (no contraction, IEEE division and square root),
 //     so the results match a scalar reference bit for bit; with the pipelined
 //     schedule this costs no time (the ALU work hides under the HBM traffic);
-//   - the overflow flag is a wave-level ballot followed by one atomic per
-//     wave that saw a non-finite sum; the flag word holds the epoch of the
-//     call that raised it, so it never has to be cleared between calls;
+//   - the overflow flag is a block-level OR followed by one counting atomic
+//     per block; the last block to finish writes the decision into a pinned
+//     host word, and on overflow into the device flag word, which holds the
+//     epoch of the call that raised it, so it never has to be cleared;
 //   - ping-pong state (read set A, write set B) makes the step a single pass:
 //     the commit is the host flipping the live set once the flag is known.
 #include "vec16.hpp"
@@ -128,10 +129,26 @@ __device__ __forceinline__ void store_half8(uint16_t* dst, const float p[8]) {
     }
 }
 
-__device__ __forceinline__ void raise_flag(const StepLaunch& a, bool bad) {
-    // every lane of every wave reaches this point
-    const unsigned long long ballot = __ballot(bad);
-    if (ballot != 0ull && (threadIdx.x & 63) == 0) atomicMax(a.flag, a.epoch);
+// End of a flag-raising pass; every thread of every block calls it.  Each
+// block ORs its threads' flags and adds (1 << 32) | block_flag to the 64-bit
+// counter word with one relaxed atomic (a single location, so the counts
+// cannot be reordered).  The block that completes the count knows the
+// result: it sets the device flag word to `epoch` on overflow (the in-place
+// update pass reads it), rearms the counter for the next launch and writes
+// (epoch << 1) | flag into the pinned host word, so the host learns the
+// decision without a copy or a stream synchronisation.
+__device__ __forceinline__ void finish_pass(const StepLaunch& a, bool bad) {
+    const int block_bad = __syncthreads_or(bad ? 1 : 0);
+    if (threadIdx.x != 0) return;
+    const unsigned long long mine = (1ull << 32) | (block_bad ? 1ull : 0ull);
+    const unsigned long long before =
+        __hip_atomic_fetch_add(a.done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((before >> 32) != gridDim.x - 1) return;
+    const bool flag = ((before & 0xFFFFFFFFull) != 0) || block_bad;
+    if (flag) atomicMax(a.flag, a.epoch);
+    __hip_atomic_store(a.done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long word = (static_cast<unsigned long long>(a.epoch) << 1) | (flag ? 1ull : 0ull);
+    __hip_atomic_store(a.host_word, word, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // The fused step.  kFlag: compute and raise the overflow flag.  kSkip: in
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
         a.v_out[e] = v;
         a.out16[e] = uint16_t(f2h(p));
     }
-    if (kFlag) raise_flag(a, bad);
+    if (kFlag) finish_pass(a, bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel_tiled(const StepLaunch a
             a.out16[e] = uint16_t(f2h(p));
         }
     }
-    if (kFlag) raise_flag(a, bad);
+    if (kFlag) finish_pass(a, bad);
 }
 
 // In-place pass 1: overflow check over the contributions alone.  A sum of at
@@ -340,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const StepLaunch a) {
             bad |= (a.grad[r][e] & 0x7C00u) == 0x7C00u;
         }
     }
-    raise_flag(a, bad);
+    finish_pass(a, bad);
 }
 
 template <int OUT>

@@ -95,13 +95,20 @@ struct StepLaunch {
     float weight_decay;
     uint32_t* flag;     // device word; set to `epoch` when a value is not finite
     uint32_t epoch;
+    unsigned long long* done;        // device word, 0 between launches: blocks finished
+                                     // (high 32 bits) and blocks that saw a non-finite
+                                     // value (low 32 bits) in the current pass
+    unsigned long long* host_word;   // pinned host word: (epoch << 1) | flag, written by
+                                     // the last block of a flag-raising pass
 };
 
 // One pass: reduce + finite check + Adam + fp16 cast, reading set *_in and
-// writing set *_out (distinct buffers); raises the flag.
+// writing set *_out (distinct buffers); raises the flag and publishes it to
+// the host word.
 hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream);
 
-// In-place mode, pass 1: finite check over the R contributions only.
+// In-place mode, pass 1: finite check over the R contributions only; raises
+// the flag and publishes it to the host word.
 hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream);
 
 // In-place mode, pass 2: the update, skipped by every thread when the flag

@@ -168,6 +168,31 @@ def test_kernel_timing_api():
     zp.set_kernel_timing(True)
     with pytest.raises(zp.ZeroError, match="STATE"):
         zp.last_kernel_ms()
+    assert zp.kernel_times() == []
     zp.set_kernel_timing(False)
     ls.step(host_contribs(rng, S, 2, 1024.0))      # untimed calls still work
     assert ls.bit_exact
+
+
+def test_kernel_times_back_to_back():
+    """zero_kernel_times: one duration per call timed back to back, oldest
+    first, the last one equal to zero_last_kernel_ms; cleared by disabling."""
+    import torch
+    import sharded_zero_partition_amd as zp
+    rng = np.random.default_rng(14)
+    S = 1 << 20
+    p0 = _p0(rng, S).cuda()
+    st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0),
+                       torch.empty_like(p0), torch.empty_like(p0), torch.empty_like(p0))
+    g = [torch.zeros(S, dtype=torch.int16, device="cuda") for _ in range(2)]
+    slot = torch.empty(S, dtype=torch.int16, device="cuda")
+    sc = zp.LossScaler.make(1024.0)
+    hpc = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    zp.set_kernel_timing(True)
+    for _ in range(5):
+        assert zp.shard_step(st, g, hpc, sc, slot) == 0
+    times = zp.kernel_times()
+    assert len(times) == 5 and all(0.0 < t < 1000.0 for t in times)
+    assert zp.last_kernel_ms() == times[-1]
+    zp.set_kernel_timing(False)
+    assert zp.kernel_times() == [] and st.t == 5
