@@ -9,8 +9,9 @@ check, applies Adam to its fp32 master/momentum/variance shard and writes the
 fp16 parameters into its slot of a 64-slot gather buffer (25.7 GB).  All
 inputs are synthetic and resident in HBM before the timed region.
 
-A timed step is one zero_shard_step call (fused kernel, the overflow decision
-that its last block publishes to the host, loss-scale control).  The same run also reports
+A timed step is one zero_shard_step call through a PreparedStep (arguments
+checked once; fused kernel, the overflow decision that its last block
+publishes to the host, loss-scale control).  The same run also reports
   * the partition layout of the 484-tensor model (host, once per model),
   * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
   * the owners' share of the bucketed reduce of two ranks' copies of that
@@ -148,8 +149,9 @@ def main():
         cpu_inputs = (p0[:cpu_n].cpu().numpy().copy(),
                       [g[:cpu_n].cpu().numpy().view(np.uint16).copy() for g in grads])
 
+    step = zp.PreparedStep(st, grads, hp, scaler, slot)   # arguments checked once
     for _ in range(args.warmup):
-        zp.shard_step(st, grads, hp, scaler, slot)
+        step()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps
@@ -158,7 +160,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        flags += zp.shard_step(st, grads, hp, scaler, slot)
+        flags += step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kernel_ms = zp.kernel_times()          # one event pair per step, read after the loop
@@ -176,7 +178,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
-    del st, grads, gather, slot, p0, arena
+    del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
 
     if args.calibration_copy:

@@ -9,7 +9,7 @@ fallback.  `workloads` holds the synthetic workload shapes and seeded input
 generators; `build` compiles the library.
 """
 
-__all__ = ["partition_layout", "Layout", "ShardState", "shard_step", "AdamHParams",
+__all__ = ["partition_layout", "Layout", "ShardState", "shard_step", "PreparedStep", "AdamHParams",
            "LossScaler", "ZeroError", "version", "device_info", "set_kernel_timing",
            "last_kernel_ms", "kernel_times", "carve_arena", "ArenaPlan"]
 

@@ -199,6 +199,9 @@ class Layout:
                                          int(align), int(bucket), _ref(h)))
         self._h = h
         self._bound = None
+        info = self.info            # fixed for the handle's life
+        self._bucket_elems = info.bucket_elems
+        self._shard_elems = info.shard_elems
 
     def close(self):
         if self._h:
@@ -265,7 +268,7 @@ class Layout:
 
     def pack_bucket(self, fill: int, bucket, stream=None) -> int:
         """Write fill `fill` into the device bucket (B two-byte elements)."""
-        if bucket.numel() != self.info.bucket_elems:
+        if bucket.numel() != self._bucket_elems:
             raise ValueError("bucket must hold bucket_elems elements")
         n = ctypes.c_int64()
         _check(lib.zero_pack_bucket(self._h, int(fill), ctypes.c_void_p(_dev_ptr(bucket, "bucket", 2)),
@@ -290,7 +293,7 @@ class Layout:
     def reduce_to_owner(self, fill: int, rank: int, shard, stream=None) -> int:
         """Write rank `rank`'s share of fill `fill` of the reduce into its fp16
         gradient shard (S two-byte elements); returns the elements written."""
-        if shard.numel() != self.info.shard_elems:
+        if shard.numel() != self._shard_elems:
             raise ValueError("shard must hold shard_elems elements")
         n = ctypes.c_int64()
         _check(lib.zero_reduce_to_owner(self._h, int(fill), int(rank),
@@ -373,6 +376,48 @@ def shard_step(state: ShardState, grads, hparams: AdamHParams, scaler: LossScale
     state.t = c.t
     state.cur = c.cur
     return flag.value
+
+
+class PreparedStep:
+    """zero_shard_step with its arguments checked and marshalled once, for
+    loops that step the same tensors again and again.
+
+    The object keeps references to the tensors; their storage must not be
+    moved or resized while it is in use.  The stream is the one given (or
+    torch's current stream) at preparation.  Every call writes state.cur and
+    state.t into the C state first and reads them back after, updates the
+    scaler in place and returns the overflow flag, like shard_step."""
+
+    def __init__(self, state: ShardState, grads, hparams: AdamHParams, scaler: LossScaler,
+                 out_slot, stream=None):
+        R = len(grads)
+        S = state.shard_elems
+        self._dev = _current_device()
+        self._ptrs = (ctypes.c_void_p * max(1, R))()
+        for r, g in enumerate(grads):
+            if g.numel() != S:
+                raise ValueError(f"grads[{r}] has {g.numel()} elements, expected {S}")
+            self._ptrs[r] = _dev_ptr(g, f"grads[{r}]", 2, self._dev) if S else None
+        if out_slot.numel() != S:
+            raise ValueError(f"out_slot has {out_slot.numel()} elements, expected {S}")
+        self._c = state._to_c(self._dev)
+        self._flag = ctypes.c_int32()
+        slot = ctypes.c_void_p(_dev_ptr(out_slot, "out_slot", 2, self._dev) if S else None)
+        self._args = (_ref(self._c), self._ptrs, R, _ref(hparams), _ref(scaler), slot,
+                      _stream_ptr(stream), _ref(self._flag))
+        self._state = state
+        self._keep = (list(grads), hparams, scaler, out_slot)
+
+    def __call__(self) -> int:
+        if _current_device() != self._dev:
+            raise ValueError(f"prepared on cuda:{self._dev}, the current device is another")
+        st, c = self._state, self._c
+        c.cur = st.cur
+        c.t = st.t
+        _check(lib.zero_shard_step(*self._args))
+        st.t = c.t
+        st.cur = c.cur
+        return self._flag.value
 
 
 def version() -> int:

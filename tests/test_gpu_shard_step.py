@@ -196,3 +196,43 @@ def test_kernel_times_back_to_back():
     assert zp.last_kernel_ms() == times[-1]
     zp.set_kernel_timing(False)
     assert zp.kernel_times() == [] and st.t == 5
+
+
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+def test_prepared_step_matches_shard_step(pingpong):
+    """PreparedStep: the same results, bit for bit, as shard_step on a copy of
+    the state, over taken and skipped steps, with cur/t written back."""
+    import torch
+    import sharded_zero_partition_amd as zp
+    rng = np.random.default_rng(15)
+    S, R = 70_001, 2
+    p0 = _p0(rng, S).cuda()
+
+    def make():
+        alt = [torch.empty_like(p0) for _ in range(3)] if pingpong else [None] * 3
+        return zp.ShardState(p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0), *alt)
+
+    sa, sb = make(), make()
+    ga = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(R)]
+    gb = [torch.empty(S, dtype=torch.int16, device="cuda") for _ in range(R)]
+    slot_a = torch.empty(S, dtype=torch.int16, device="cuda")
+    slot_b = torch.empty(S, dtype=torch.int16, device="cuda")
+    hpc = zp.AdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    sca, scb = zp.LossScaler.make(1024.0), zp.LossScaler.make(1024.0)
+    prepared = zp.PreparedStep(sb, gb, hpc, scb, slot_b)
+    for k in range(6):
+        contribs = host_contribs(rng, S, R, 1024.0)
+        if k == 3:
+            contribs[1][S // 2] = 0x7C00          # +inf: this step is skipped
+        for g_dev in (ga, gb):
+            for r in range(R):
+                g_dev[r].copy_(contribs[r])
+        fa = zp.shard_step(sa, ga, hpc, sca, slot_a)
+        fb = prepared()
+        assert fa == fb == (1 if k == 3 else 0)
+        assert (sa.t, sa.cur) == (sb.t, sb.cur)
+        assert (sca.scale, sca.good_steps) == (scb.scale, scb.good_steps)
+        for x, y in zip(sa.live(), sb.live()):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert torch.equal(slot_a, slot_b)
+    assert sb.t == 5
