@@ -19,6 +19,7 @@ publishes to the host, loss-scale control).  The same run also reports
   * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
     HIP-event time on its stream) and, when the counter profile under
     profiles/ was taken from the current kernel source, its measured traffic,
+  * a plain 2 GiB device copy as the achievable-bandwidth line,
   * the CPU oracle timed on the host on a bounded sample of the same shard.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
@@ -72,7 +73,8 @@ def parse_args():
     ap.add_argument("--no-pack", action="store_true", help="skip the bucket-pack measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run a plain 2 GiB device copy (scale reference for HBM counters)")
+                    help="three more plain 2 GiB device copies after the copy probe (the scale "
+                         "reference of the HBM counter runs)")
     ap.add_argument("--pack-views", action="store_true",
                     help="pack sources as views of one buffer instead of 20,000 allocations")
     ap.add_argument("--arena", action="store_true",
@@ -181,14 +183,25 @@ def main():
     del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
 
-    if args.calibration_copy:
-        a = torch.empty(1 << 30, dtype=torch.int16, device=dev)   # 2 GiB
-        b = torch.empty_like(a)
-        a.fill_(1)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    # the achievable line: a plain device copy of 2 GiB (read 2 GiB, write 2 GiB),
+    # timed with HIP events; also the reference dispatch for the counter scale
+    a = torch.empty(1 << 30, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    copy_ms = []
+    for _ in range(5 + (3 if args.calibration_copy else 0)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    del a, b
+    copy_gbs = 2 * 2 * (1 << 30) / (float(np.median(copy_ms)) * 1e-3) / 1e9
+    copy_probe = {"achieved": round(copy_gbs, 1), "unit": "GB/s",
+                  "what": "torch copy_ of a 2 GiB tensor into another (4 GiB moved), median of "
+                          f"{len(copy_ms)}, HIP events",
+                  "step_frac_of_copy": round(achieved / copy_gbs, 4)}
 
     # a2: bucket pack of the 20,000-tensor stream
     pack = None
@@ -301,6 +314,7 @@ def main():
         "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
+        "copy_probe": copy_probe,
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
         "reduce_to_owner": reduce_owner,
