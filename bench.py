@@ -19,7 +19,7 @@ publishes to the host, loss-scale control).  The same run also reports
   * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
     HIP-event time on its stream) and, when the counter profile under
     profiles/ was taken from the current kernel source, its measured traffic,
-  * a plain 2 GiB device copy as the achievable-bandwidth line,
+  * torch's device copy of 2 GiB for comparison (a library copy kernel),
   * the CPU oracle timed on the host on a bounded sample of the same shard.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
@@ -183,8 +183,9 @@ def main():
     del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
 
-    # the achievable line: a plain device copy of 2 GiB (read 2 GiB, write 2 GiB),
-    # timed with HIP events; also the reference dispatch for the counter scale
+    # a library copy for comparison: torch's copy_ of 2 GiB (read 2 GiB, write
+    # 2 GiB), timed with HIP events; also the reference dispatch for the
+    # counter scale
     a = torch.empty(1 << 30, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
@@ -198,10 +199,10 @@ def main():
         copy_ms.append(e0.elapsed_time(e1))
     del a, b
     copy_gbs = 2 * 2 * (1 << 30) / (float(np.median(copy_ms)) * 1e-3) / 1e9
-    copy_probe = {"achieved": round(copy_gbs, 1), "unit": "GB/s",
-                  "what": "torch copy_ of a 2 GiB tensor into another (4 GiB moved), median of "
-                          f"{len(copy_ms)}, HIP events",
-                  "step_frac_of_copy": round(achieved / copy_gbs, 4)}
+    library_copy = {"achieved": round(copy_gbs, 1), "unit": "GB/s",
+                    "what": "torch copy_ of a 2 GiB tensor into another (4 GiB moved), median "
+                            f"of {len(copy_ms)}, HIP events",
+                    "step_over_copy": round(achieved / copy_gbs, 4)}
 
     # a2: bucket pack of the 20,000-tensor stream
     pack = None
@@ -314,7 +315,7 @@ def main():
         "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
-        "copy_probe": copy_probe,
+        "library_copy": library_copy,
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
         "reduce_to_owner": reduce_owner,
