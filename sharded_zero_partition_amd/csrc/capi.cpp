@@ -71,10 +71,6 @@ int blocks_per_cu_tiled() {
     return v;
 }
 
-int blocks_per_cu_pack() {
-    static const int v = env_int("ZERO_PACK_BLOCKS_PER_CU", 8, 1, 4096);
-    return v;
-}
 
 namespace {
 

@@ -38,7 +38,6 @@ struct zero_layout {
     int32_t* d_first = nullptr;
     int32_t n_src = 0;
     int32_t chunk_shift = 0;
-    int cu_count = 0;
 
     // device tables of the reduce-to-owner (zero_layout_bind_contributions)
     int r_device = -1;
@@ -370,11 +369,8 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
-    int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_tensors");
+    const int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_tensors");
     if (rc != ZERO_OK) return rc;
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return zp::fail_hip(e, "hipDeviceGetAttribute");
 
     zp::PackSrc* d_src = nullptr;
     int32_t* d_first = nullptr;
@@ -404,7 +400,6 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     l->n_src = int32_t(src.size());
     l->chunk_shift = shift;
     l->device = dev;
-    l->cu_count = cus;
     return ZERO_OK;
 }
 
@@ -437,7 +432,7 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     hipStream_t st = static_cast<hipStream_t>(stream);
     e = zp::timing_begin(st);
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");
-    e = zp::launch_pack(a, l->cu_count, st);
+    e = zp::launch_pack(a, st);
     if (e != hipSuccess) return zp::fail_hip(e, "pack kernel launch");
     e = zp::timing_end(st);
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");

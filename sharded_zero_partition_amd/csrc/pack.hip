@@ -193,8 +193,7 @@ constexpr int kPackSpanU = 2;
 
 }  // namespace
 
-hipError_t launch_pack(const PackLaunch& a, int cu_count, hipStream_t stream) {
-    (void)cu_count;
+hipError_t launch_pack(const PackLaunch& a, hipStream_t stream) {
     constexpr int64_t kSpan = 512 * kPackSpanU;
     const int64_t waves = (a.bucket_elems + kSpan - 1) / kSpan;
     int64_t blocks = (waves + 3) / 4;

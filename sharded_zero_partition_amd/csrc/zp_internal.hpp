@@ -42,7 +42,7 @@ struct PackLaunch {
     uint16_t* bucket;         // device, 16-byte aligned
 };
 
-hipError_t launch_pack(const PackLaunch& a, int cu_count, hipStream_t stream);
+hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // bucket reduce-to-owner
@@ -128,11 +128,10 @@ int check_stream_device(void* stream, int dev, const char* what);
 hipError_t timing_begin(hipStream_t stream);
 hipError_t timing_end(hipStream_t stream);
 
-// Launch shape knobs (blocks per CU of the grid-stride kernels), read once
-// from ZERO_BLOCKS_PER_CU / ZERO_TILED_BLOCKS_PER_CU / ZERO_PACK_BLOCKS_PER_CU
-// when set.
+// Launch shape knobs (blocks per CU of the grid-stride and the pipelined step
+// kernels), read once from ZERO_BLOCKS_PER_CU / ZERO_TILED_BLOCKS_PER_CU when
+// set.
 int blocks_per_cu_step();
 int blocks_per_cu_tiled();
-int blocks_per_cu_pack();
 
 }  // namespace zp
