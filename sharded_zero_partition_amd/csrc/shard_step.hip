@@ -15,12 +15,11 @@
 //
 // Every element is independent and the kernel moves 26 + 2R bytes per element
 // for about 80 ALU operations, so it is bound by HBM bandwidth.  Design:
-//   - R = 1, 2, 4: a persistent grid (one 256-thread block per CU) whose waves
-//     walk 1024-element tiles with a register double buffer -- the loads of
-//     the next tile are in flight while the current one is computed -- and
-//     fully coalesced 128/64-bit accesses (step_kernel_tiled); other R: a
-//     grid-stride loop over 8-element vectors (step_kernel); a scalar tail
-//     for the elements past the last whole tile or vector;
+//   - a persistent grid (one 256-thread block per CU) whose waves walk tiles
+//     of 1024, 512 or 256 elements (by R) with a register double buffer --
+//     the loads of the next tile are in flight while the current one is
+//     computed -- and fully coalesced 128/64-bit accesses; a scalar tail for
+//     the elements past the last whole tile;
 //   - the fp32 arithmetic is written in the order of the definition with one
 //     rounding per operation (no contraction, IEEE division and square root),
 //     so the results match a scalar reference bit for bit; with the pipelined
@@ -79,34 +78,12 @@ __device__ __forceinline__ void adam_element(const StepLaunch& a, float sum, flo
     v = vi;
 }
 
-// Sum of the R contributions for 8 consecutive elements starting at e0.
-// R == 0 selects the run-time count a.R (1..16).
-template <int R>
-__device__ __forceinline__ void reduce8(const StepLaunch& a, int64_t e0, float s[8]) {
-    const u32x4 c0 = load_stream(reinterpret_cast<const u32x4*>(a.grad[0] + e0));
-    const uint32_t w0[4] = {c0.x, c0.y, c0.z, c0.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s[k] = h2f(w0[k >> 1] >> (16 * (k & 1)));
-    constexpr int kMax = R == 0 ? kMaxContrib : R;
-#pragma unroll
-    for (int r = 1; r < kMax; ++r) {
-        if (R == 0 && r >= a.R) break;
-        const u32x4 c = load_stream(reinterpret_cast<const u32x4*>(a.grad[r] + e0));
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s[k] = s[k] + h2f(w[k >> 1] >> (16 * (k & 1)));
-    }
-}
-
+// Sum of the R contributions of element e, contribution 0 first.
 template <int R>
 __device__ __forceinline__ float reduce1(const StepLaunch& a, int64_t e) {
     float s = h2f(a.grad[0][e]);
-    constexpr int kMax = R == 0 ? kMaxContrib : R;
 #pragma unroll
-    for (int r = 1; r < kMax; ++r) {
-        if (R == 0 && r >= a.R) break;
-        s = s + h2f(a.grad[r][e]);
-    }
+    for (int r = 1; r < R; ++r) s = s + h2f(a.grad[r][e]);
     return s;
 }
 
@@ -151,85 +128,38 @@ __device__ __forceinline__ void finish_pass(const StepLaunch& a, bool bad) {
     __hip_atomic_store(a.host_word, word, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// The fused step.  kFlag: compute and raise the overflow flag.  kSkip: in
-// place, after the check pass -- do nothing if the flag holds this epoch.
-template <int R, int OUT, bool kFlag, bool kSkip>
-__global__ __launch_bounds__(kThreads) void step_kernel(const StepLaunch a) {
-    if (kSkip && __atomic_load_n(a.flag, __ATOMIC_RELAXED) == a.epoch) return;
-    const int64_t nvec = a.n >> 3;
-    const int64_t stride = int64_t(gridDim.x) * kThreads;
-    const int64_t tid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-    bool bad = false;
-    for (int64_t i = tid; i < nvec; i += stride) {
-        const int64_t e0 = i << 3;
-        float s[8];
-        reduce8<R>(a, e0, s);
-        const f32x4 p0 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0));
-        const f32x4 p1 = load_stream(reinterpret_cast<const f32x4*>(a.p_in + e0 + 4));
-        const f32x4 m0 = load_stream(reinterpret_cast<const f32x4*>(a.m_in + e0));
-        const f32x4 m1 = load_stream(reinterpret_cast<const f32x4*>(a.m_in + e0 + 4));
-        const f32x4 v0 = load_stream(reinterpret_cast<const f32x4*>(a.v_in + e0));
-        const f32x4 v1 = load_stream(reinterpret_cast<const f32x4*>(a.v_in + e0 + 4));
-        float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (kFlag) bad |= not_finite(s[k]);
-            adam_element(a, s[k], p[k], m[k], v[k]);
-        }
-        store_stream(reinterpret_cast<f32x4*>(a.p_out + e0), f32x4{p[0], p[1], p[2], p[3]});
-        store_stream(reinterpret_cast<f32x4*>(a.p_out + e0 + 4), f32x4{p[4], p[5], p[6], p[7]});
-        store_stream(reinterpret_cast<f32x4*>(a.m_out + e0), f32x4{m[0], m[1], m[2], m[3]});
-        store_stream(reinterpret_cast<f32x4*>(a.m_out + e0 + 4), f32x4{m[4], m[5], m[6], m[7]});
-        store_stream(reinterpret_cast<f32x4*>(a.v_out + e0), f32x4{v[0], v[1], v[2], v[3]});
-        store_stream(reinterpret_cast<f32x4*>(a.v_out + e0 + 4), f32x4{v[4], v[5], v[6], v[7]});
-        store_half8<OUT>(a.out16 + e0, p);
-    }
-    // the last S mod 8 elements, one per thread
-    const int64_t tail = a.n - (nvec << 3);
-    if (tid < tail) {
-        const int64_t e = (nvec << 3) + tid;
-        const float s = reduce1<R>(a, e);
-        if (kFlag) bad |= not_finite(s);
-        float p = a.p_in[e], m = a.m_in[e], v = a.v_in[e];
-        adam_element(a, s, p, m, v);
-        a.p_out[e] = p;
-        a.m_out[e] = m;
-        a.v_out[e] = v;
-        a.out16[e] = uint16_t(f2h(p));
-    }
-    if (kFlag) finish_pass(a, bad);
+// ---------------------------------------------------------------------------
+// The step kernel (every R from 1 to 16).
+//
+// Each wave owns tiles of 256 H elements, tile t covering [256 H t,
+// 256 H (t+1)).  Lane l holds elements 4l..4l+3 of each of the tile's H
+// 256-element groups, so every load and store instruction of the wave
+// touches one contiguous 1 KiB (fp32) or 512 B (fp16) range.  The grid is
+// persistent (one 256-thread block per CU) and each wave walks its tiles with
+// a register double buffer: the loads of the next tile are in flight while
+// the current tile is computed and stored, so the ALU work overlaps the
+// memory traffic instead of adding to it.  H shrinks as R grows so that the
+// two buffers fit the register file: 4 up to R = 4 (1024-element tiles, which
+// measured 2.5% faster than 512 at R = 2; more waves per SIMD were slower),
+// 2 up to R = 8, 1 beyond.
+// ---------------------------------------------------------------------------
+
+template <int R>
+constexpr int halves_for() {
+    return R <= 4 ? 4 : (R <= 8 ? 2 : 1);
 }
 
-// ---------------------------------------------------------------------------
-// Pipelined variant for R = 1, 2, 4 (the common counts).
-//
-// Each wave owns tiles of kTile = 1024 elements, tile t covering
-// [kTile t, kTile (t+1)).  Lane l holds elements 4l..4l+3 of each of the
-// tile's four 256-element groups, so every load and store instruction of the
-// wave touches one contiguous 1 KiB (fp32) or 512 B (fp16) range.  The grid is persistent (a few waves per SIMD) and
-// each wave walks its tiles with a register double buffer: the loads of the
-// next tile are in flight while the current tile is computed and stored, so
-// the ALU work overlaps the memory traffic instead of adding to it.  (One
-// wave per SIMD with 1024-element tiles measured best: 512-element tiles were
-// 2.5% slower, more waves per SIMD slower still.)
-// ---------------------------------------------------------------------------
-
-constexpr int kHalves = 4;             // 256-element groups per tile (4: 186 VGPRs)
-constexpr int kTile = 256 * kHalves;
-
-template <int R>
+template <int R, int H>
 struct TileRegs {
-    u32x2 g[R][kHalves];   // 4 fp16 values per group, per contribution
-    f32x4 p[kHalves], m[kHalves], v[kHalves];
+    u32x2 g[R][H];   // 4 fp16 values per group, per contribution
+    f32x4 p[H], m[H], v[H];
 };
 
-template <int R>
+template <int R, int H>
 __device__ __forceinline__ void load_tile(const StepLaunch& a, int64_t base, int lane,
-                                          TileRegs<R>& t) {
+                                          TileRegs<R, H>& t) {
 #pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
+    for (int h = 0; h < H; ++h) {
         const int64_t e = base + h * 256 + 4 * lane;
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -257,11 +187,11 @@ __device__ __forceinline__ void store_half4(uint16_t* dst, const float p[4]) {
     }
 }
 
-template <int R, int OUT, bool kFlag>
+template <int R, int H, int OUT, bool kFlag>
 __device__ __forceinline__ void compute_tile(const StepLaunch& a, int64_t base, int lane,
-                                             const TileRegs<R>& t, bool& bad) {
+                                             const TileRegs<R, H>& t, bool& bad) {
 #pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
+    for (int h = 0; h < H; ++h) {
         const int64_t e = base + h * 256 + 4 * lane;
         float s[4];
         const uint32_t w0[2] = {t.g[0][h].x, t.g[0][h].y};
@@ -288,25 +218,29 @@ __device__ __forceinline__ void compute_tile(const StepLaunch& a, int64_t base, 
     }
 }
 
-template <int R, int OUT, bool kFlag, bool kSkip>
+// kFlag: compute the overflow flag and hand it over (the fused pass).
+// kSkip: in place, after the check pass -- do nothing if the flag holds this
+// call's epoch.
+template <int R, int H, int OUT, bool kFlag, bool kSkip>
 __global__ __launch_bounds__(kThreads) void step_kernel_tiled(const StepLaunch a) {
     if (kSkip && __atomic_load_n(a.flag, __ATOMIC_RELAXED) == a.epoch) return;
+    constexpr int64_t kTile = 256 * H;
     const int lane = threadIdx.x & 63;
     const int64_t ntiles = a.n / kTile;
     const int64_t waves = int64_t(gridDim.x) * (kThreads / 64);
     int64_t t = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
     bool bad = false;
-    TileRegs<R> A, B;
-    if (t < ntiles) load_tile<R>(a, t * kTile, lane, A);
+    TileRegs<R, H> A, B;
+    if (t < ntiles) load_tile<R, H>(a, t * kTile, lane, A);
     while (t < ntiles) {
         int64_t tn = t + waves;
-        if (tn < ntiles) load_tile<R>(a, tn * kTile, lane, B);
-        compute_tile<R, OUT, kFlag>(a, t * kTile, lane, A, bad);
+        if (tn < ntiles) load_tile<R, H>(a, tn * kTile, lane, B);
+        compute_tile<R, H, OUT, kFlag>(a, t * kTile, lane, A, bad);
         t = tn;
         if (t >= ntiles) break;
         tn = t + waves;
-        if (tn < ntiles) load_tile<R>(a, tn * kTile, lane, A);
-        compute_tile<R, OUT, kFlag>(a, t * kTile, lane, B, bad);
+        if (tn < ntiles) load_tile<R, H>(a, tn * kTile, lane, A);
+        compute_tile<R, H, OUT, kFlag>(a, t * kTile, lane, B, bad);
         t = tn;
     }
     // the last S mod kTile elements: block 0, one element per thread per pass
@@ -398,38 +332,40 @@ dim3 grid_for(int64_t n, int cu_count, int per_cu) {
 
 template <bool kFlag, bool kSkip, int R>
 void launch_tiled_r(const StepLaunch& a, int cu_count, hipStream_t s) {
-    const int64_t ntiles = a.n / kTile;
+    constexpr int H = halves_for<R>();
+    const int64_t ntiles = a.n / (256 * H);
     int64_t blocks = (ntiles + 3) / 4;
     const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * blocks_per_cu_tiled();
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;   // block 0 also owns the tail
     const dim3 grid{unsigned(blocks)};
     switch (out_class(a.out16)) {
-        case kOut16B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut8B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut4B: hipLaunchKernelGGL((step_kernel_tiled<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_kernel_tiled<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-    }
-}
-
-template <bool kFlag, bool kSkip, int R>
-void launch_step_r(const StepLaunch& a, dim3 grid, hipStream_t s) {
-    switch (out_class(a.out16)) {
-        case kOut16B: hipLaunchKernelGGL((step_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut8B: hipLaunchKernelGGL((step_kernel<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut4B: hipLaunchKernelGGL((step_kernel<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_kernel<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut16B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut8B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut4B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
     }
 }
 
 template <bool kFlag, bool kSkip>
 void launch_step(const StepLaunch& a, int cu_count, hipStream_t s) {
-    const dim3 grid = grid_for(a.n, cu_count, blocks_per_cu_step());
     switch (a.R) {
         case 1: launch_tiled_r<kFlag, kSkip, 1>(a, cu_count, s); break;
         case 2: launch_tiled_r<kFlag, kSkip, 2>(a, cu_count, s); break;
+        case 3: launch_tiled_r<kFlag, kSkip, 3>(a, cu_count, s); break;
         case 4: launch_tiled_r<kFlag, kSkip, 4>(a, cu_count, s); break;
-        default: launch_step_r<kFlag, kSkip, 0>(a, grid, s); break;
+        case 5: launch_tiled_r<kFlag, kSkip, 5>(a, cu_count, s); break;
+        case 6: launch_tiled_r<kFlag, kSkip, 6>(a, cu_count, s); break;
+        case 7: launch_tiled_r<kFlag, kSkip, 7>(a, cu_count, s); break;
+        case 8: launch_tiled_r<kFlag, kSkip, 8>(a, cu_count, s); break;
+        case 9: launch_tiled_r<kFlag, kSkip, 9>(a, cu_count, s); break;
+        case 10: launch_tiled_r<kFlag, kSkip, 10>(a, cu_count, s); break;
+        case 11: launch_tiled_r<kFlag, kSkip, 11>(a, cu_count, s); break;
+        case 12: launch_tiled_r<kFlag, kSkip, 12>(a, cu_count, s); break;
+        case 13: launch_tiled_r<kFlag, kSkip, 13>(a, cu_count, s); break;
+        case 14: launch_tiled_r<kFlag, kSkip, 14>(a, cu_count, s); break;
+        case 15: launch_tiled_r<kFlag, kSkip, 15>(a, cu_count, s); break;
+        default: launch_tiled_r<kFlag, kSkip, 16>(a, cu_count, s); break;
     }
 }
 
