@@ -19,7 +19,7 @@ def test_random_cases():
     rng = np.random.default_rng(2024)
     for case in range(40):
         S = int(rng.choice([1, 5, 511, 1023, 1024, 1025, 4096, 33333, 123457]))
-        R = int(rng.integers(1, 9))
+        R = int(rng.integers(1, 17))
         pingpong = bool(rng.integers(0, 2))
         off = int(rng.integers(0, 8))
         scale = float(2.0 ** rng.integers(0, 17))
