@@ -38,7 +38,7 @@ __device__ __forceinline__ u32x4 gather8(const PackSrc* __restrict__ src, int i,
         const int64_t ge = g + e;
         if (e < nvalid && ge < psi) {
             while (ge >= src[i].flat_off + src[i].len) ++i;
-            const uint32_t val = src[i].ptr[ge - src[i].flat_off];
+            const uint32_t val = ld2(src[i].ptr + (ge - src[i].flat_off));
             w[e >> 1] |= val << (16 * (e & 1));
         }
     }
@@ -104,9 +104,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
             u32x4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                v[u] = *reinterpret_cast<const u32x4*>(base0 + 512 * u + 8 * lane);
+                v[u] = ld16(base0 + 512 * u + 8 * lane);
             u32x4 extra = v[U - 1];
-            if (ph) extra = *reinterpret_cast<const u32x4*>(base0 + kSpan);
+            if (ph) extra = ld16(base0 + kSpan);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 u32x4 nxt;
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (mode[u] == 1) {
-            lo_v[u] = *reinterpret_cast<const u32x4*>(blk[u]);
+            lo_v[u] = ld16(blk[u]);
             // aligned: read the same block twice rather than past its end
-            hi_v[u] = *reinterpret_cast<const u32x4*>(blk[u] + (phase[u] ? 8 : 0));
+            hi_v[u] = ld16(blk[u] + (phase[u] ? 8 : 0));
         }
     }
 #pragma unroll

@@ -48,9 +48,9 @@ __device__ __forceinline__ int search(const int64_t* __restrict__ off, int lo, i
 // fp32 sum over the contributions of the element at offset rel of source i.
 template <int R>
 __device__ __forceinline__ float sum1(const ReduceLaunch& a, int i, int64_t rel) {
-    const int nr = R == 0 ? a.R : R;   // compile-time count unrolls fully
-    float s = h2f(a.ptr[i][rel]);
-    for (int r = 1; r < nr; ++r) s = s + h2f(a.ptr[int64_t(r) * a.n_src + i][rel]);
+    float s = h2f(ld2(a.ptr[i] + rel));
+#pragma unroll
+    for (int r = 1; r < R; ++r) s = s + h2f(ld2(a.ptr[int64_t(r) * a.n_src + i] + rel));
     return s;
 }
 
@@ -71,43 +71,61 @@ __device__ __forceinline__ u32x4 next_block(const u32x4 v[kU], int u, u32x4 extr
     return lane == 63 ? first_of_next : nxt;
 }
 
-// Cooperative span with a compile-time contribution count R: all R * kU
-// aligned blocks (plus the extra blocks) are loaded before any is used.
+// Cooperative span with a compile-time contribution count R.  The
+// contributions go in groups of up to kGroup: all of a group's kU aligned
+// blocks per lane (plus its extra blocks) are loaded before any is used, and
+// the fp32 sums carry over from group to group in contribution order.  (All
+// sixteen at once needs about 200 VGPRs and ran slower than two groups.)
+constexpr int kGroup = 4;
+
 template <int R>
-__device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_t rel0, int64_t len,
+__device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_t rel0,
                                           int64_t kw, int mis, int lane) {
-    u32x4 v[R][kU];
-    u32x4 extra[R];
-    int ph[R];
+    constexpr int G = R < kGroup ? R : kGroup;
+    float s[kU][8];
+    int64_t dep = 0;   // 0; makes a group's addresses wait for the previous group's sums
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint16_t* t = a.ptr[int64_t(r) * a.n_src + src];
-        const uint16_t* p0 = t + rel0;
-        ph[r] = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
-        const uint16_t* b0 = p0 - ph[r];
+    for (int r0 = 0; r0 < R; r0 += G) {
+        u32x4 v[G][kU];
+        u32x4 extra[G];
+        int ph[G];
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-            v[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane));
-        // aligned: re-read the last group's block rather than past the span
-        extra[r] = *reinterpret_cast<const u32x4*>(b0 + (ph[r] ? 8 * kSpanVec : 512 * (kU - 1) + 8 * lane));
-    }
-    (void)len;
+        for (int j = 0; j < G; ++j) {
+            if (r0 + j >= R) break;
+            const uint16_t* t = a.ptr[int64_t(r0 + j) * a.n_src + src];
+            const uint16_t* p0 = t + rel0;
+            ph[j] = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+            const uint16_t* b0 = p0 - ph[j] + dep;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        float s[8];
+            for (int u = 0; u < kU; ++u)
+                v[j][u] = ld16_stream(b0 + 512 * u + 8 * lane);
+            // aligned: re-read the last group's block rather than past the span
+            extra[j] = ld16(b0 + (ph[j] ? 8 * kSpanVec : 512 * (kU - 1) + 8 * lane));
+        }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const u32x4 wv = window8(v[r][u], next_block(v[r], u, extra[r], lane), ph[r]);
-            const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+        for (int u = 0; u < kU; ++u) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
-                s[e] = r == 0 ? x : s[e] + x;
+            for (int j = 0; j < G; ++j) {
+                if (r0 + j >= R) break;
+                const u32x4 wv = window8(v[j][u], next_block(v[j], u, extra[j], lane), ph[j]);
+                const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
+                    s[u][e] = r0 + j == 0 ? x : s[u][e] + x;
+                }
             }
         }
+        // The next group's loads may not start before this group's sums
+        // exist: an empty asm statement takes a sum and yields `dep`, which
+        // stays 0 but is opaque to the compiler, and the next addresses add it.
+        if (r0 + G < R) asm volatile("" : "+v"(dep) : "v"(s[0][0]));
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
         uint32_t o[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = f2h(s[2 * d]) | (f2h(s[2 * d + 1]) << 16);
+        for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
         const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
         __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(a.shard + jv));
     }
@@ -115,7 +133,7 @@ __device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaunch a) {
-    const int nr = R == 0 ? a.R : R;   // contributions; compile-time unless R == 0
+    constexpr int nr = R;   // contributions (compile-time: every loop over them unrolls)
     const int lane = threadIdx.x & 63;
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wave_in_block;
@@ -159,57 +177,8 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
             in_bounds = in_bounds && b0 >= t && b0 + need <= t + one_len;
         }
         if (in_bounds) {
-            if (R > 0) {
-                // compile-time count: every contribution's loads are issued
-                // before the first shuffle
-                coop_span<R == 0 ? 1 : R>(a, lo, rel0, one_len, kw, mis, lane);
-                return;
-            }
-            float s[kU][8];
-            for (int r = 0; r < nr; ++r) {
-                const uint16_t* t = a.ptr[int64_t(r) * a.n_src + lo];
-                const uint16_t* p0 = t + rel0;
-                const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
-                const uint16_t* b0 = p0 - ph;
-                u32x4 v[kU];
-#pragma unroll
-                for (int u = 0; u < kU; ++u)
-                    v[u] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(b0 + 512 * u + 8 * lane));
-                u32x4 extra = v[kU - 1];
-                if (ph) extra = *reinterpret_cast<const u32x4*>(b0 + 8 * kSpanVec);
-#pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    u32x4 nxt;
-                    nxt.x = __shfl_down(v[u].x, 1);
-                    nxt.y = __shfl_down(v[u].y, 1);
-                    nxt.z = __shfl_down(v[u].z, 1);
-                    nxt.w = __shfl_down(v[u].w, 1);
-                    const u32x4 head = u + 1 < kU ? v[u + 1 < kU ? u + 1 : u] : extra;
-                    u32x4 first_of_next;
-                    first_of_next.x = __shfl(head.x, 0);
-                    first_of_next.y = __shfl(head.y, 0);
-                    first_of_next.z = __shfl(head.z, 0);
-                    first_of_next.w = __shfl(head.w, 0);
-                    if (lane == 63) nxt = first_of_next;
-                    const u32x4 wv = window8(v[u], nxt, ph);
-                    const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
-                        s[u][e] = r == 0 ? x : s[u][e] + x;
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                uint32_t o[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
-                const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
-                __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
-                                            reinterpret_cast<u32x4*>(a.shard + jv));
-            }
+            // every contribution's loads are issued before the first shuffle
+            coop_span<R>(a, lo, rel0, kw, mis, lane);
             return;
         }
     }
@@ -227,8 +196,10 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
             const int64_t rel = g0 - soff;
             if (rel + 8 <= slen) {
                 float s[8];
+                int64_t dep = 0;   // as in coop_span: groups of kGroup contributions
+#pragma unroll
                 for (int r = 0; r < nr; ++r) {
-                    const uint16_t* t = a.ptr[int64_t(r) * a.n_src + i];
+                    const uint16_t* t = a.ptr[int64_t(r) * a.n_src + i + dep];
                     const u32x4 v = load8(t + rel, t, t + slen);
                     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -236,6 +207,7 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
                         const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
                         s[e] = r == 0 ? x : s[e] + x;
                     }
+                    if ((r + 1) % kGroup == 0 && r + 1 < nr) asm volatile("" : "+v"(dep) : "v"(s[0]));
                 }
                 uint32_t o[4];
 #pragma unroll
@@ -244,7 +216,9 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
                 continue;
             }
         }
-        // range ends and tensor boundaries: element by element
+        // range ends and tensor boundaries: element by element (rare; kept
+        // rolled so that its loads do not set the kernel's register count)
+#pragma unroll 1
         for (int e = 0; e < 8; ++e) {
             const int64_t j = jv + e;
             if (j < j_lo || j >= j_hi) continue;
@@ -269,8 +243,20 @@ hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream) {
     switch (a.R) {
         case 1: hipLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
         case 2: hipLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(reduce_owner_kernel<3>, grid, dim3(kThreads), 0, stream, a); break;
         case 4: hipLaunchKernelGGL(reduce_owner_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(reduce_owner_kernel<0>, grid, dim3(kThreads), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL(reduce_owner_kernel<5>, grid, dim3(kThreads), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL(reduce_owner_kernel<6>, grid, dim3(kThreads), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL(reduce_owner_kernel<7>, grid, dim3(kThreads), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(reduce_owner_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+        case 9: hipLaunchKernelGGL(reduce_owner_kernel<9>, grid, dim3(kThreads), 0, stream, a); break;
+        case 10: hipLaunchKernelGGL(reduce_owner_kernel<10>, grid, dim3(kThreads), 0, stream, a); break;
+        case 11: hipLaunchKernelGGL(reduce_owner_kernel<11>, grid, dim3(kThreads), 0, stream, a); break;
+        case 12: hipLaunchKernelGGL(reduce_owner_kernel<12>, grid, dim3(kThreads), 0, stream, a); break;
+        case 13: hipLaunchKernelGGL(reduce_owner_kernel<13>, grid, dim3(kThreads), 0, stream, a); break;
+        case 14: hipLaunchKernelGGL(reduce_owner_kernel<14>, grid, dim3(kThreads), 0, stream, a); break;
+        case 15: hipLaunchKernelGGL(reduce_owner_kernel<15>, grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(reduce_owner_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
     }
     return hipGetLastError();
 }

@@ -41,21 +41,39 @@ __device__ __forceinline__ u32x4 window8(u32x4 a, u32x4 b, int ph) {
     }
 }
 
+// Device buffers reached through a table of pointers arrive as generic
+// pointers, for which the compiler emits flat loads (address-space check,
+// 64-bit VGPR addresses, and a second wait counter shared with LDS and scalar
+// loads).  Every buffer here is device global memory, so reads go through
+// these global-address-space views instead.
+typedef __attribute__((address_space(1))) const u32x4 GlobalU32x4;
+typedef __attribute__((address_space(1))) const uint16_t GlobalU16;
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {    // 16-byte aligned
+    return *(const GlobalU32x4*)(p);   // address-space cast
+}
+__device__ __forceinline__ u32x4 ld16_stream(const uint16_t* p) {   // non-temporal
+    return __builtin_nontemporal_load((const GlobalU32x4*)(p));
+}
+__device__ __forceinline__ uint32_t ld2(const uint16_t* p) {
+    return *(const GlobalU16*)(p);
+}
+
 // Eight consecutive fp16 patterns starting at p, read as aligned 16-byte
 // blocks only when those blocks lie inside [lo, hi) (the tensor holding p);
 // otherwise element by element.  Requires [p, p + 8) inside [lo, hi).
 __device__ __forceinline__ u32x4 load8(const uint16_t* p, const uint16_t* lo, const uint16_t* hi) {
     const int ph = int((reinterpret_cast<uintptr_t>(p) & 15) >> 1);
     const uint16_t* base = p - ph;
-    if (ph == 0) return *reinterpret_cast<const u32x4*>(p);
+    if (ph == 0) return ld16(p);
     if (base >= lo && base + 16 <= hi) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(base);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(base + 8);
+        const u32x4 a = ld16(base);
+        const u32x4 b = ld16(base + 8);
         return window8(a, b, ph);
     }
     uint32_t w[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) w[d] = uint32_t(p[2 * d]) | (uint32_t(p[2 * d + 1]) << 16);
+    for (int d = 0; d < 4; ++d) w[d] = ld2(p + 2 * d) | (ld2(p + 2 * d + 1) << 16);
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 

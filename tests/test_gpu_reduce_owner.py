@@ -37,7 +37,7 @@ def _lists(rng, numels, R):
     return out
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 9, 16])
 def test_small_all_fills_and_owners(R):
     rng = np.random.default_rng(100 + R)
     for trial in range(4):
