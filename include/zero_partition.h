@@ -190,6 +190,9 @@ int zero_arena_plan_for(const zero_layout* layout, int32_t pingpong, int32_t n_c
  * `stream`; the call waits for the upload).
  *   dev_ptrs  host array of n_tensors device pointers to fp16 data, each
  *             2-byte aligned; NULL entries are allowed for zero-sized tensors.
+ *             Pointer i must address at least numel[i] elements (the sizes
+ *             the layout was built with): the pack reads exactly that many,
+ *             and device sizes cannot be checked here.
  * The tensors must stay allocated while the layout is used for packing.
  * Binding again replaces the previous table.  Errors: STATE (layout has no
  * bucket plan), INVALID_ARG, ALIGNMENT, HIP, OUT_OF_MEMORY. */
@@ -216,7 +219,9 @@ int zero_pack_bucket(const zero_layout* layout, int64_t fill, uint16_t* bucket,
  *   R         1..16
  *   dev_ptrs  host array of R * n_tensors device pointers to fp16 data; row r
  *             (entries r*n_tensors ... r*n_tensors + n_tensors - 1) holds rank
- *             r's tensors; each 2-byte aligned; NULL allowed for empty ones.
+ *             r's tensors; each 2-byte aligned; NULL allowed for empty ones;
+ *             each must address at least numel[i] elements, as for
+ *             zero_layout_bind_tensors.
  * Uploads the tables on the current device (the call waits for the upload).
  * The tensors must stay allocated while the layout reduces.  Binding again
  * replaces the previous contribution table; the pack binding is separate.

@@ -8,9 +8,13 @@ when the library has not been built (`python -m sharded_zero_partition_amd.build
 
 Names follow the C ABI in include/zero_partition.h:
   partition_layout(...)   -> Layout   (zero_partition_layout and accessors)
+  Layout.arena_plan(...)               (zero_arena_plan_for); carve_arena(plan)
   Layout.bind_tensors(...)             (zero_layout_bind_tensors)
   Layout.pack_bucket(...)              (zero_pack_bucket)
-  shard_step(...)                      (zero_shard_step)
+  Layout.bind_contributions(...)       (zero_layout_bind_contributions)
+  Layout.reduce_to_owner(...)          (zero_reduce_to_owner)
+  shard_step(...), PreparedStep(...)   (zero_shard_step)
+  set_kernel_timing, last_kernel_ms, kernel_times   (kernel timing)
 """
 
 import ctypes
@@ -199,6 +203,7 @@ class Layout:
                                          int(align), int(bucket), _ref(h)))
         self._h = h
         self._bound = None
+        self._numels = [int(n) for n in numels]
         info = self.info            # fixed for the handle's life
         self._bucket_elems = info.bucket_elems
         self._shard_elems = info.shard_elems
@@ -257,9 +262,19 @@ class Layout:
                                        int(bool(with_bucket)), int(align_bytes), _ref(out)))
         return out
 
+    def _check_list(self, tensors, what: str):
+        """The library reads numel[i] elements from tensor i: the list must
+        match the layout's tensor count and sizes exactly."""
+        if len(tensors) != len(self._numels):
+            raise ValueError(f"{what} has {len(tensors)} tensors, the layout {len(self._numels)}")
+        for i, (t, n) in enumerate(zip(tensors, self._numels)):
+            if t.numel() != n:
+                raise ValueError(f"{what}: tensor {i} has {t.numel()} elements, the layout {n}")
+
     def bind_tensors(self, tensors, stream=None):
         """Bind the device fp16 tensors (any 2-byte dtype, contiguous) in
         list order; they must stay alive while packing."""
+        self._check_list(tensors, "tensor list")
         ptrs = (ctypes.c_void_p * max(1, len(tensors)))()
         for i, t in enumerate(tensors):
             ptrs[i] = _dev_ptr(t, f"tensor {i}", 2) if t.numel() > 0 else None
@@ -275,16 +290,14 @@ class Layout:
                                     _stream_ptr(stream), _ref(n)))
         return n.value
 
-
     def bind_contributions(self, lists, stream=None):
         """Bind R lists of device fp16 tensors (one list per reducing rank, in
         the layout's tensor order) for reduce_to_owner."""
         R = len(lists)
-        nt = self.info.n_tensors
+        nt = len(self._numels)
         ptrs = (ctypes.c_void_p * max(1, R * nt))()
         for r, lst in enumerate(lists):
-            if len(lst) != nt:
-                raise ValueError(f"list {r} has {len(lst)} tensors, the layout {nt}")
+            self._check_list(lst, f"list {r}")
             for i, t in enumerate(lst):
                 ptrs[r * nt + i] = _dev_ptr(t, f"tensor {r}/{i}", 2) if t.numel() > 0 else None
         _check(lib.zero_layout_bind_contributions(self._h, R, ptrs, _stream_ptr(stream)))

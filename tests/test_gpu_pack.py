@@ -90,6 +90,11 @@ def test_errors():
     big = torch.zeros(24, dtype=torch.int16, device="cuda")
     with pytest.raises(zp.ZeroError, match="ALIGNMENT"):
         lay.pack_bucket(0, big[1:17])                 # bucket must be 16-byte aligned
+    # the binding checks the list against the layout before the library reads it
+    with pytest.raises(ValueError, match="tensors, the layout"):
+        lay.bind_tensors(t[:1])
+    with pytest.raises(ValueError, match="elements, the layout"):
+        lay.bind_tensors([t[0], t[1][:-1]])
 
 
 def test_pack_20k_full_size():

@@ -85,6 +85,8 @@ def test_errors():
         lay.bind_contributions([lists[0]] * 17)           # R <= 16
     with pytest.raises(zp.ZeroError, match="STATE"):
         zp.partition_layout(numels, 2).bind_contributions(lists)   # no bucket plan
+    with pytest.raises(ValueError, match="elements, the layout"):
+        lay.bind_contributions([lists[0], [lists[1][0][:-1], lists[1][1]]])
     # psi = 30, S = 15, B = 16: fill 1 is [16, 30), rank 0 owns [0, 15)
     assert lay.reduce_to_owner(1, 0, shard) == 0
     assert lay.reduce_to_owner(0, 1, shard) == 1          # flat index 15 only
