@@ -172,7 +172,8 @@ def main():
 
     step_ms = elapsed / args.steps * 1e3
     value = S * args.steps / elapsed
-    bytes_per_elem = 26 + 2 * R
+    # ping-pong: one pass; in place: the check pass reads the contributions once more
+    bytes_per_elem = 26 + 2 * R if args.mode == "pingpong" else 26 + 4 * R
     alg_bytes = bytes_per_elem * S
     kern_avg_ms = float(np.mean(kernel_ms))
     achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
