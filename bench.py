@@ -73,8 +73,8 @@ def parse_args():
     ap.add_argument("--no-pack", action="store_true", help="skip the bucket-pack measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--calibration-copy", action="store_true",
-                    help="three more plain 2 GiB device copies after the copy probe (the scale "
-                         "reference of the HBM counter runs)")
+                    help="three more plain 2 GiB device copies after the library copy (the "
+                         "scale reference of the HBM counter runs)")
     ap.add_argument("--pack-views", action="store_true",
                     help="pack sources as views of one buffer instead of 20,000 allocations")
     ap.add_argument("--arena", action="store_true",
@@ -177,7 +177,7 @@ def main():
     alg_bytes = bytes_per_elem * S
     kern_avg_ms = float(np.mean(kernel_ms))
     achieved = alg_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(S)
+    traffic = measured_traffic(S) if args.mode == "pingpong" else None   # profile is of the fused pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
