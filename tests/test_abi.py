@@ -155,7 +155,7 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(g=(ctypes.c_void_p * 2)(None, base + 20480)) == -1
     assert call(slot=ctypes.c_void_p(base + 100)) == -1               # overlaps p
     st2 = zp.ShardStateC.from_buffer_copy(st)
-    st2.p[1] = base + 1 << 20                                        # partial ping-pong set
+    st2.p[1] = base + (1 << 20)                                      # partial ping-pong set
     assert call(st=st2) == -1
     st3 = zp.ShardStateC.from_buffer_copy(st)
     st3.cur = 1                                                      # cur = 1 in place
@@ -165,9 +165,23 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(st=st4) == -2
     assert zp.lib.zero_shard_step(None, grads, 2, ctypes.byref(hp), ctypes.byref(sc), slot, None,
                                   None) == -1
-    assert b"R must be" in zp.lib.zero_last_error() or True
+    assert b"NULL state" in zp.lib.zero_last_error()
     # nothing was modified
     assert sc.scale == 1024.0 and st.t == 0
+
+
+def test_kernel_timing_calls_need_no_device(zp):
+    """The timing calls keep per-thread host state only until a timed call
+    records events: before that they answer without a GPU."""
+    lib = zp.lib
+    n = ctypes.c_int64(-1)
+    ms = ctypes.c_float()
+    assert lib.zero_set_kernel_timing(1) == 0
+    assert lib.zero_last_kernel_ms(ctypes.byref(ms)) == -7            # STATE: nothing timed
+    assert lib.zero_kernel_times(None, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.zero_kernel_times(None, 0, None) == -1
+    assert lib.zero_last_kernel_ms(None) == -1
+    assert lib.zero_set_kernel_timing(0) == 0
 
 
 def test_reduce_to_owner_argument_errors_need_no_device(zp):
