@@ -13,6 +13,8 @@ A timed step is one zero_shard_step call through a PreparedStep (arguments
 checked once; fused kernel, the overflow decision that its last block
 publishes to the host, loss-scale control).  The same run also reports
   * the partition layout of the 484-tensor model (host, once per model),
+  * the rank's whole local share of an iteration: its full gradient stream
+    packed through a 2^26 bucket, then the shard step,
   * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
   * the owners' share of the bucketed reduce of two ranks' copies of that
     stream into the 16 owners' fp16 gradient shards,
@@ -75,6 +77,8 @@ def parse_args():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="three more plain 2 GiB device copies after the library copy (the "
                          "scale reference of the HBM counter runs)")
+    ap.add_argument("--no-rank-iteration", action="store_true",
+                    help="skip the 13B rank's full gradient-stream pack + step measurement")
     ap.add_argument("--pack-views", action="store_true",
                     help="pack sources as views of one buffer instead of 20,000 allocations")
     ap.add_argument("--arena", action="store_true",
@@ -180,6 +184,45 @@ def main():
     traffic = measured_traffic(S) if args.mode == "pingpong" else None   # profile is of the fused pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    # The rank's whole local share of one iteration at 13B: its full fp16
+    # gradient stream (the model's 484 tensors, packed bucket by bucket for the
+    # reduce-scatter) through a 2^26-element bucket, then the shard step.
+    rank_iteration = None
+    if not args.no_pack and not args.no_rank_iteration:
+        gB = 1 << 26
+        glay = zp.partition_layout(w.numels, w.n_ranks, stage=w.stage, bucket=gB)
+        gstream = [torch.empty(n, dtype=torch.float16, device=dev).normal_(0.0, 1e-3 * w.scale)
+                   .view(torch.int16) for n in w.numels]
+        glay.bind_tensors(gstream)
+        gbucket = torch.empty(gB, dtype=torch.int16, device=dev)
+        n_fills = glay.info.n_fills
+
+        def iteration():
+            for k in range(n_fills):
+                glay.pack_bucket(k, gbucket)
+            return step()
+
+        flags += iteration()
+        torch.cuda.synchronize()
+        iters = 3
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            flags += iteration()
+        torch.cuda.synchronize()
+        it_s = (time.perf_counter() - t0) / iters
+        assert flags == 0, "unexpected overflow in the benchmark inputs"
+        psi = sum(w.numels)
+        it_bytes = 4 * psi + 2 * (n_fills * gB - psi) + bytes_per_elem * S
+        rank_iteration = {
+            "workload": f"zero3_13b rank 63: the full fp16 gradient stream ({len(w.numels)} tensors, "
+                        f"{psi} elements) packed through a 2^26 bucket ({n_fills} fills), then the "
+                        "shard step",
+            "ms": round(it_s * 1e3, 3),
+            "algorithmic_gbs": round(it_bytes / it_s / 1e9, 1),
+            "frac": round(it_bytes / it_s / 1e9 / HBM_PEAK_GBS, 4)}
+        glay.close()
+        del gstream, gbucket
 
     del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
@@ -323,6 +366,7 @@ def main():
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
         "library_copy": library_copy,
+        "rank_iteration": rank_iteration,
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
         "reduce_to_owner": reduce_owner,
