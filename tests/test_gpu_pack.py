@@ -112,3 +112,38 @@ def test_pack_20k_views_full_size():
     w = W.pack_20k()
     tensors = W.pack_sources(w, device="cuda", views=True)
     _check_all_fills(tensors, w.numels, w.bucket, n_ranks=w.n_ranks)
+
+
+def test_13b_gradient_stream_sampled_fills():
+    """The 13B model's full fp16 gradient stream (484 tensors, 12.85e9
+    elements, 192 fills of 2^26) as the benchmark's rank iteration packs it:
+    the first fill, the one holding the boundary after the token embedding,
+    a middle one and the ragged last one, each against the oracle's window of
+    the tensors it overlaps (copied to the host slice by slice)."""
+    w = W.zero3_13b()
+    B = 1 << 26
+    numels = w.numels
+    print(f"[13B stream] tensors={len(numels)} psi={sum(numels)}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    tensors = [torch.randint(-32768, 32768, (n,), dtype=torch.int16, device="cuda", generator=gen)
+               for n in numels]
+    lay = zp.partition_layout(numels, w.n_ranks, stage=w.stage, bucket=B)
+    lay.bind_tensors(tensors)
+    n_fills = lay.info.n_fills
+    assert n_fills == 192
+    offs = np.concatenate([[0], np.cumsum(numels)]).astype(np.int64)
+    b = torch.empty(B, dtype=torch.int16, device="cuda")
+    for k in (0, int(offs[1]) // B, n_fills // 2, n_fills - 1):
+        lo, hi = k * B, (k + 1) * B
+        # the slices of the tensors that meet [lo, hi), in list order
+        pieces = []
+        for i, n in enumerate(numels):
+            a, z = max(lo, int(offs[i])), min(hi, int(offs[i]) + n)
+            if a < z:
+                pieces.append(tensors[i][a - int(offs[i]):z - int(offs[i])].cpu().numpy().view(np.uint16))
+        want = oracle.flat_window(pieces, 0, B)
+        lay.pack_bucket(k, b)
+        got = b.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), f"fill {k}"
+    lay.close()
