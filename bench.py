@@ -328,6 +328,7 @@ def main():
 
     # CPU oracle on a bounded sample of the same shard (first step's inputs)
     cpu = None
+    cpu_threads = None
     if cpu_inputs is not None:
         import oracle
         p_host, c_host = cpu_inputs
@@ -341,6 +342,31 @@ def main():
                "kind": "oracle",
                "sample": f"the whole rank-63 shard ({cpu_n} elements), first step "
                          f"(scalar C oracle, one thread, {cpu_s:.1f} s)"}
+
+        # The same C functions over contiguous chunks in parallel threads (the
+        # calls release the GIL): the overflow flag over every chunk first,
+        # then Adam on every chunk when no chunk overflowed.
+        from concurrent.futures import ThreadPoolExecutor
+        n_threads = max(1, min(16, os.cpu_count() or 1))
+        bounds = np.linspace(0, cpu_n, n_threads + 1).astype(np.int64)
+        par = oracle.ShardState(p_host)
+        par_out = np.empty(cpu_n, np.uint16)
+        ohp = oracle.AdamHP(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
+        parts = [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(n_threads) as pool:
+            flags_par = list(pool.map(lambda ab: oracle.overflow_flag([c[ab[0]:ab[1]] for c in c_host]), parts))
+            if not any(flags_par):
+                list(pool.map(lambda ab: oracle.adam_apply(
+                    [c[ab[0]:ab[1]] for c in c_host], par.p[ab[0]:ab[1]], par.m[ab[0]:ab[1]],
+                    par.v[ab[0]:ab[1]], par_out[ab[0]:ab[1]], w.scale, 1, ohp), parts))
+        par_s = time.perf_counter() - t0
+        assert np.array_equal(par_out, out16) and np.array_equal(par.p.view(np.uint32), ost.p.view(np.uint32))
+        cpu_threads = {"value": round(cpu_n / par_s, 1), "unit": "elements/s", "cores": n_threads,
+                       "kind": "oracle",
+                       "sample": f"the same shard and step, the oracle's C functions over {len(parts)} "
+                                 f"contiguous chunks in {n_threads} threads ({par_s:.2f} s); results "
+                                 "equal to the one-thread run"}
 
     out = {
         "metric": METRIC,
@@ -371,6 +397,7 @@ def main():
         "pack": pack,
         "reduce_to_owner": reduce_owner,
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_threads,
     }
     print(json.dumps(out), flush=True)
 
