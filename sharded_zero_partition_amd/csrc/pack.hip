@@ -11,15 +11,16 @@
 // matter how ragged the tensors are.  A wave owns a span of 512 U elements
 // (U = 2) and lane l the vectors at 512 u + 8 l, so each store instruction
 // writes 1 KiB contiguously.  The wave reads the source range of its span
-// from a chunk index built at bind time (chunk = one span), through the
-// scalar cache; when the span lies in one tensor (almost always) no search is
-// needed, otherwise each lane binary-searches the few candidates.  When the
-// 8 elements of a vector come from one tensor the lane reads one aligned
-// 128-bit block, or two and a funnel shift when the source is misaligned
-// (the second block is the neighbour lane's first, so it hits in cache); the
-// loads of all U vectors are issued before any is used.  Vectors that
-// straddle tensors, touch a tensor edge or the end of the stream are gathered
-// element by element.  No LDS: each wave's accesses are already contiguous.
+// from a chunk index built at bind time (one entry per 2^shift >= 2048
+// elements), through the scalar cache.  When the whole span lies in one
+// tensor (almost always) the misalignment phase is wave-uniform: each lane
+// loads one aligned 128-bit block per vector and takes the following block
+// from its neighbour lane by cross-lane shuffle.  Otherwise each lane
+// binary-searches the few candidate tensors, reads one aligned block (two and
+// a funnel shift when misaligned) for a vector inside one tensor, and issues
+// the loads of all U vectors before any is used; vectors that straddle
+// tensors, touch a tensor edge or the end of the stream are gathered element
+// by element.  No LDS staging: each wave's accesses are already contiguous.
 #include "vec16.hpp"
 #include "zp_internal.hpp"
 
