@@ -234,7 +234,9 @@ int zero_layout_bind_contributions(zero_layout* layout, int32_t R,
  *   shard[g - rank*S] = fp16( c_0(g) + c_1(g) + ... + c_{R-1}(g) )
  * where c_r is rank r's bound tensor list laid back to back in list order,
  * the sum is formed in fp32 from contribution 0 up and rounded once to fp16
- * (nearest, ties to even).  Every other element of `shard` is left as it is.
+ * (nearest, ties to even); an infinite sum is written as fp16 infinity and a
+ * NaN sum as an fp16 NaN (its payload bits are not specified).  Every other
+ * element of `shard` is left as it is.
  *   shard    device, the owner's fp16 gradient shard (S values), 2-byte aligned
  *   written  optional host output: elements written (0 when the fill and the
  *            rank's shard do not meet)

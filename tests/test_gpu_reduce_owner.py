@@ -123,3 +123,37 @@ def test_pack_20k_two_ranks_full_size():
     flats = [np.concatenate(h) for h in host]
     vals = oracle.float_to_half(oracle.reduce([f[idx] for f in flats]))
     assert np.array_equal(got[idx], vals)
+
+
+def test_special_values_in_contributions():
+    """Overflowed gradients reach the reduce before the step's flag sees them:
+    +-inf and NaN inputs give exactly the oracle's infinities, NaN wherever
+    the oracle has NaN (payload bits unspecified), and every finite sum bit
+    for bit."""
+    rng = np.random.default_rng(31)
+    numels = [1000, 37, 4096 + 5, 3]
+    R = 3
+    lists = _lists(rng, numels, R)
+    specials = np.array([0x7C00, 0xFC00, 0x7E00, 0x7C01], np.uint16).view(np.int16)
+    for lst in lists:
+        for t in lst:
+            n = t.numel()
+            pos = torch.from_numpy(rng.integers(0, n, size=max(1, n // 50)))
+            t[pos.cuda()] = torch.from_numpy(rng.choice(specials, size=pos.numel())).cuda()
+    lay = zp.partition_layout(numels, 2, stage=2, bucket=777)
+    olay = OL.partition_layout(numels, 2, 2, 1, 777)
+    lay.bind_contributions(lists)
+    host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+    S = olay.shard
+    for r in range(2):
+        shard = torch.full((S,), SENT, dtype=torch.int16, device="cuda")
+        want = np.full(S, SENT, np.uint16)
+        for k in range(olay.n_fills):
+            lay.reduce_to_owner(k, r, shard)
+            off, vals = oracle.reduce_to_owner(host, olay, k, r)
+            want[off:off + vals.size] = vals
+        got = shard.cpu().numpy().view(np.uint16)
+        nan = lambda x: ((x & 0x7C00) == 0x7C00) & ((x & 0x3FF) != 0)   # noqa: E731
+        assert np.array_equal(nan(got), nan(want))
+        assert nan(want).any() and ((want & 0x7FFF) == 0x7C00).any()  # the case holds both
+        assert np.array_equal(got[~nan(want)], want[~nan(want)])
