@@ -267,6 +267,8 @@ typedef struct zero_shard_state {
     int64_t t;             /* Adam steps taken so far (skipped steps excluded) */
 } zero_shard_state;
 
+/* All finite; beta1, beta2 in [0, 1); eps > 0 (with eps = 0 a zero gradient
+ * on a zero variance would divide 0 by 0). */
 typedef struct zero_adam_hparams {
     float lr;
     float beta1;

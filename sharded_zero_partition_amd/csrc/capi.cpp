@@ -254,9 +254,11 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         !(sc->growth > 0.0f) || !zp::finite_f(sc->min_scale) || sc->min_scale < 0.0f ||
         sc->growth_interval < 0 || sc->good_steps < 0)
         return fail(ZERO_ERR_INVALID_ARG, "invalid loss-scaler settings");
-    if (!zp::finite_f(hp->lr) || !zp::finite_f(hp->eps) || !zp::finite_f(hp->weight_decay) ||
+    if (!zp::finite_f(hp->lr) || !zp::finite_f(hp->eps) || !(hp->eps > 0.0f) ||
+        !zp::finite_f(hp->weight_decay) ||
         !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(ZERO_ERR_INVALID_ARG, "invalid Adam hyper-parameters (betas must be in [0, 1))");
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "invalid Adam hyper-parameters (finite; eps > 0; betas in [0, 1))");
 
     if (S > 0) {
         if (!grads) return fail(ZERO_ERR_INVALID_ARG, "grads is NULL");

@@ -148,6 +148,7 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(R=0) == -1 and call(R=17) == -1
     assert call(hp=zp.AdamHParams(1e-4, 1.0, 0.999, 1e-8, 0.0)) == -1
     assert call(hp=zp.AdamHParams(float("nan"), 0.9, 0.999, 1e-8, 0.0)) == -1
+    assert call(hp=zp.AdamHParams(1e-4, 0.9, 0.999, 0.0, 0.0)) == -1       # eps must be > 0
     assert call(sc=zp.LossScaler.make(0.0)) == -1
     assert call(sc=zp.LossScaler.make(float("inf"))) == -1
     assert call(slot=ctypes.c_void_p(base + 24577)) == -2             # slot odd address
