@@ -42,7 +42,7 @@ METRIC = ("fused shard-step elements/s and achieved HBM GB/s (% of peak) per ran
 HBM_PEAK_GBS = 8000.0
 PMC_PROFILE = os.path.join(ROOT, "profiles", "shard_step_zero3_13b_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "sharded_zero_partition_amd", "csrc", f)
-                  for f in ("shard_step.hip", "zp_internal.hpp", "vec16.hpp")]
+                  for f in ("shard_step.hip", "zp_internal.hpp", "vec16.hpp", "adam.hpp")]
 
 
 def kernel_source_hash() -> str:

@@ -30,6 +30,7 @@
 //     epoch of the call that raised it, so it never has to be cleared;
 //   - ping-pong state (read set A, write set B) makes the step a single pass:
 //     the commit is the host flipping the live set once the flag is known.
+#include "adam.hpp"
 #include "vec16.hpp"
 #include "zp_internal.hpp"
 
@@ -49,10 +50,6 @@ constexpr int kOut8B = 1;
 constexpr int kOut4B = 2;
 constexpr int kOut2B = 3;
 
-__device__ __forceinline__ bool not_finite(float x) {
-    return (__builtin_bit_cast(uint32_t, x) & 0x7F800000u) == 0x7F800000u;
-}
-
 template <typename T>
 __device__ __forceinline__ T load_stream(const T* p) {
     return __builtin_nontemporal_load(p);
@@ -61,21 +58,6 @@ __device__ __forceinline__ T load_stream(const T* p) {
 template <typename T>
 __device__ __forceinline__ void store_stream(T* p, T v) {
     __builtin_nontemporal_store(v, p);
-}
-
-// Textbook Adam on one element, one rounding per operation.
-__device__ __forceinline__ void adam_element(const StepLaunch& a, float sum, float& p, float& m,
-                                             float& v) {
-    float g = sum * a.inv_scale;
-    if (a.weight_decay != 0.0f) g = g + a.weight_decay * p;
-    const float mi = a.beta1 * m + a.one_minus_beta1 * g;
-    const float vi = a.beta2 * v + a.one_minus_beta2 * (g * g);
-    const float mhat = mi / a.bias_corr1;
-    const float vhat = vi / a.bias_corr2;
-    const float den = __builtin_sqrtf(vhat) + a.eps;
-    p = p - a.lr * (mhat / den);
-    m = mi;
-    v = vi;
 }
 
 // Sum of the R contributions of element e, contribution 0 first.
