@@ -18,6 +18,8 @@ publishes to the host, loss-scale control).  The same run also reports
   * the bucket pack of the 20,000-tensor stream (82 fills of 2^26),
   * the owners' share of the bucketed reduce of two ranks' copies of that
     stream into the 16 owners' fp16 gradient shards,
+  * the owner step: rank 63's shard step fed straight from two ranks' whole
+    gradient streams of the 13B model (reduce and update in one pass),
   * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
     HIP-event time on its stream) and, when the counter profile under
     profiles/ was taken from the current kernel source, its measured traffic,
@@ -79,6 +81,8 @@ def parse_args():
                          "scale reference of the HBM counter runs)")
     ap.add_argument("--no-rank-iteration", action="store_true",
                     help="skip the 13B rank's full gradient-stream pack + step measurement")
+    ap.add_argument("--no-owner-step", action="store_true",
+                    help="skip the owner-step measurement (shard step fed from the ranks' tensor lists)")
     ap.add_argument("--pack-views", action="store_true",
                     help="pack sources as views of one buffer instead of 20,000 allocations")
     ap.add_argument("--arena", action="store_true",
@@ -226,6 +230,53 @@ def main():
 
     del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
+
+    # NEXT: the owner step -- the same rank's shard step with its sum taken
+    # straight from R = 2 ranks' whole gradient streams of the model (484
+    # tensors each, one buffer per rank with 0..7-element gaps), so the
+    # Stage 2 reduce of its partition and the update are one pass
+    owner = None
+    if not args.no_owner_step:
+        olay = zp.partition_layout(w.numels, w.n_ranks, stage=w.stage, bucket=1 << 26)
+        streams = [W.gradient_stream(w.numels, w.wid, r, w.scale, 1, dev) for r in range(R)]
+        olay.bind_contributions([views for _, _, views in streams])
+        n_real = max(0, min(S, sum(w.numels) - w.rank * S))
+        op0 = W.master_init(w, device=dev)
+        ost = zp.ShardState(op0, torch.zeros_like(op0), torch.zeros_like(op0),
+                            torch.empty_like(op0), torch.empty_like(op0), torch.empty_like(op0))
+        oslot = torch.empty(S, dtype=torch.int16, device=dev)
+        oscaler = zp.LossScaler.make(w.scale)
+        oflags = 0
+        for _ in range(args.warmup):
+            oflags += olay.owner_step(w.rank, ost, hp, oscaler, oslot)
+        torch.cuda.synchronize()
+        zp.set_kernel_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            oflags += olay.owner_step(w.rank, ost, hp, oscaler, oslot)
+        torch.cuda.synchronize()
+        o_wall = (time.perf_counter() - t0) / args.steps
+        o_ms = zp.kernel_times()
+        zp.set_kernel_timing(False)
+        assert len(o_ms) == args.steps and oflags == 0
+        o_kern = float(np.mean(o_ms)) * 1e-3
+        o_bytes = (26 + 2 * R) * n_real           # R fp16 reads, p/m/v in and out, fp16 slot
+        o_gbs = o_bytes / o_kern / 1e9
+        owner = {
+            "workload": f"zero3_13b rank 63: R = {R} ranks' whole fp16 gradient streams "
+                        f"({len(w.numels)} tensors each, misaligned in one buffer per rank) "
+                        "reduced straight into the ping-pong Adam step of the rank's "
+                        f"{n_real} real elements",
+            "elements": n_real,
+            "ms_per_step": round(o_wall * 1e3, 4),
+            "kernel_ms": round(o_kern * 1e3, 4),
+            "kernel_ms_min": round(float(np.min(o_ms)), 4),
+            "fused_step_kernel_ms": round(kern_avg_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(o_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(o_gbs / HBM_PEAK_GBS, 4)}}
+        olay.close()
+        del streams, ost, op0, oslot
+        torch.cuda.empty_cache()
 
     # a library copy for comparison: torch's copy_ of 2 GiB (read 2 GiB, write
     # 2 GiB), timed with HIP events; also the reference dispatch for the
@@ -396,6 +447,7 @@ def main():
         "layout_ms": round(layout_ms, 3),
         "pack": pack,
         "reduce_to_owner": reduce_owner,
+        "owner_step": owner,
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_threads,
     }

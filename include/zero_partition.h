@@ -323,6 +323,35 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
                     const zero_adam_hparams* hp, zero_loss_scaler* scaler,
                     uint16_t* out_slot, void* stream, int32_t* overflow);
 
+/* Owner step: zero_shard_step in ping-pong mode with the sum taken straight
+ * from the contribution lists bound by zero_layout_bind_contributions, so the
+ * Stage 2 reduce of the rank's partition and its Stage 1 update are one pass
+ * and no fp16 gradient shard is written in between.  With n = the rank's real
+ * elements (min(S, psi - rank*S), or 0) and, for j < n,
+ *   sum(j) = c_0(rank*S + j) + ... + c_{R-1}(rank*S + j)
+ * (fp16 values, fp32 additions from contribution 0 up; c_r as for
+ * zero_reduce_to_owner), the flag, the Adam arithmetic, the slot, the skip
+ * and the loss-scale rule are those of zero_shard_step over j < n.  Elements
+ * [n, S) of the state sets and of the slot are neither read nor written; a
+ * rank with n = 0 launches nothing and takes a step (t + 1, cur flipped).
+ *   layout    bucket plan with contributions bound on the current device
+ *   rank      0 .. n_ranks - 1: whose partition is updated
+ *   st        ping-pong state (p[1], m[1], v[1] set), shard_elems = the
+ *             layout's S; 16-byte aligned, pairwise disjoint, disjoint from
+ *             every bound contribution tensor
+ *   out_slot  device, S fp16 values, 2-byte aligned (gather + rank * S)
+ *   overflow  host output: 1 if the step was skipped, else 0 (may be NULL)
+ * Returns once the overflow decision is known (a one-thread kernel after the
+ * pass writes it into the pinned host word the call polls, as for
+ * zero_shard_step); the pass, and restoring the slot of a skipped step, are
+ * ordered on `stream`.  Calls on one device are serialised by the library,
+ * together with zero_shard_step.
+ * Errors: INVALID_ARG (rank, in-place state, S mismatch, overlap),
+ * ALIGNMENT, STATE (no bucket plan, not bound, another device), HIP. */
+int zero_owner_step(const zero_layout* layout, int32_t rank, zero_shard_state* st,
+                    const zero_adam_hparams* hp, zero_loss_scaler* scaler,
+                    uint16_t* out_slot, void* stream, int32_t* overflow);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (profiling aid)                                            */
 /* ------------------------------------------------------------------------ */

@@ -14,6 +14,7 @@ Names follow the C ABI in include/zero_partition.h:
   Layout.bind_contributions(...)       (zero_layout_bind_contributions)
   Layout.reduce_to_owner(...)          (zero_reduce_to_owner)
   shard_step(...), PreparedStep(...)   (zero_shard_step)
+  Layout.owner_step(...)               (zero_owner_step)
   set_kernel_timing, last_kernel_ms, kernel_times   (kernel timing)
 """
 
@@ -120,6 +121,7 @@ SIGNATURES = {
     "zero_layout_bind_contributions": (ctypes.c_int, [_P, _I32, _P, _P]),
     "zero_reduce_to_owner": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "zero_shard_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
+    "zero_owner_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P]),
     "zero_set_kernel_timing": (ctypes.c_int, [_I32]),
     "zero_last_kernel_ms": (ctypes.c_int, [_P]),
     "zero_kernel_times": (ctypes.c_int, [_P, _I64, _P]),
@@ -313,6 +315,29 @@ class Layout:
                                         ctypes.c_void_p(_dev_ptr(shard, "shard", 2)),
                                         _stream_ptr(stream), _ref(n)))
         return n.value
+
+
+    def owner_step(self, rank: int, state: "ShardState", hparams: "AdamHParams",
+                   scaler: "LossScaler", out_slot, stream=None) -> int:
+        """zero_owner_step: rank `rank`'s ping-pong shard step with the sum
+        taken straight from the bound contribution lists.  Returns the
+        overflow flag; updates state.t, state.cur and the scaler in place."""
+        S = self._shard_elems
+        if not state.pingpong:
+            raise ValueError("the owner step needs ping-pong state (p_alt, m_alt, v_alt)")
+        if state.shard_elems != S:
+            raise ValueError(f"state holds {state.shard_elems} elements, the layout's shard {S}")
+        if out_slot.numel() != S:
+            raise ValueError(f"out_slot has {out_slot.numel()} elements, expected {S}")
+        dev = _current_device()
+        c = state._to_c(dev)
+        flag = ctypes.c_int32()
+        slot = ctypes.c_void_p(_dev_ptr(out_slot, "out_slot", 2, dev) if S else None)
+        _check(lib.zero_owner_step(self._h, int(rank), _ref(c), _ref(hparams), _ref(scaler), slot,
+                                   _stream_ptr(stream), _ref(flag)))
+        state.t = c.t
+        state.cur = c.cur
+        return flag.value
 
 
 def partition_layout(numels: Sequence[int], n_ranks: int, stage: int = 2, align: int = 1,

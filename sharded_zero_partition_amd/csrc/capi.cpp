@@ -226,6 +226,130 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool finite_f(float x) { return std::isfinite(x); }
 
+// Scalar checks shared by the step entry points (nothing is modified).
+int check_step_scalars(const zero_shard_state* st, const zero_adam_hparams* hp,
+                       const zero_loss_scaler* sc, bool* pingpong) {
+    const int64_t S = st->shard_elems;
+    if (S < 0) return fail(ZERO_ERR_INVALID_ARG, "shard_elems < 0");
+    if (S > std::numeric_limits<int64_t>::max() / 16) return fail(ZERO_ERR_INDEX_OVERFLOW, "shard too large");
+    if (st->cur != 0 && st->cur != 1) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 or 1");
+    if (st->t < 0 || st->t == std::numeric_limits<int64_t>::max())
+        return fail(ZERO_ERR_INVALID_ARG, "step count out of range");
+    const bool has1[3] = {st->p[1] != nullptr, st->m[1] != nullptr, st->v[1] != nullptr};
+    *pingpong = has1[0];
+    if (has1[1] != *pingpong || has1[2] != *pingpong)
+        return fail(ZERO_ERR_INVALID_ARG, "p[1], m[1], v[1] must be all set or all NULL");
+    if (!*pingpong && st->cur != 0) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 in place");
+    if (!std::isfinite(sc->scale) || !(sc->scale > 0.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale must be finite and > 0");
+    if (!finite_f(sc->backoff) || !(sc->backoff > 0.0f) || !finite_f(sc->growth) ||
+        !(sc->growth > 0.0f) || !finite_f(sc->min_scale) || sc->min_scale < 0.0f ||
+        sc->growth_interval < 0 || sc->good_steps < 0)
+        return fail(ZERO_ERR_INVALID_ARG, "invalid loss-scaler settings");
+    if (!finite_f(hp->lr) || !finite_f(hp->eps) || !(hp->eps > 0.0f) || !finite_f(hp->weight_decay) ||
+        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "invalid Adam hyper-parameters (finite; eps > 0; betas in [0, 1))");
+    return ZERO_OK;
+}
+
+// Pointer checks of the state sets and the slot over their first n
+// elements: non-NULL, aligned, pairwise disjoint.  Their byte ranges go to
+// rs[0 .. *nr).
+int check_state_arrays(const zero_shard_state* st, bool pingpong, const uint16_t* out_slot, int64_t n,
+                       Range rs[7], int* nr) {
+    *nr = 0;
+    const int sets = pingpong ? 2 : 1;
+    for (int k = 0; k < sets; ++k) {
+        const float* arr[3] = {st->p[k], st->m[k], st->v[k]};
+        for (const float* a : arr) {
+            if (!a) return fail(ZERO_ERR_INVALID_ARG, "a state pointer is NULL");
+            if (!aligned(a, 16)) return fail(ZERO_ERR_ALIGNMENT, "state array not 16-byte aligned");
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(a);
+            rs[(*nr)++] = {lo, lo + uintptr_t(n) * 4};
+        }
+    }
+    if (!out_slot) return fail(ZERO_ERR_INVALID_ARG, "out_slot is NULL");
+    if (!aligned(out_slot, 2)) return fail(ZERO_ERR_ALIGNMENT, "out_slot not 2-byte aligned");
+    const uintptr_t olo = reinterpret_cast<uintptr_t>(out_slot);
+    rs[(*nr)++] = {olo, olo + uintptr_t(n) * 2};
+    for (int i = 0; i < *nr; ++i)
+        for (int j = i + 1; j < *nr; ++j)
+            if (overlap(rs[i], rs[j])) return fail(ZERO_ERR_INVALID_ARG, "state arrays and slot must not overlap");
+    return ZERO_OK;
+}
+
+// Device, stream check and workspace of a step call; advances the epoch (the
+// flag words hold epochs, so after wrap-around they are cleared first).
+// The caller holds (*ws)->mu from here on through `lock`.
+int begin_step(void* stream, const char* who, DeviceWorkspace** ws, std::unique_lock<std::mutex>* lock,
+               int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    int rc = check_stream_device(stream, dev, who);
+    if (rc != ZERO_OK) return rc;
+    rc = get_workspace(dev, ws);
+    if (rc != ZERO_OK) return rc;
+    *lock = std::unique_lock<std::mutex>((*ws)->mu);
+    if (++(*ws)->epoch == 0) {
+        e = hipMemsetAsync((*ws)->d_flag, 0, sizeof(uint32_t), static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync (flag)");
+        __atomic_store_n((*ws)->h_word, 0ull, __ATOMIC_RELEASE);
+        (*ws)->epoch = 1;
+    }
+    *dev_out = dev;
+    return ZERO_OK;
+}
+
+// State pointers and Adam constants for step t + 1 (used only if the step is
+// taken); the flag words of `ws` at its current epoch.
+void step_constants(StepLaunch* a, const zero_shard_state* st, bool pingpong, const zero_adam_hparams* hp,
+                    const zero_loss_scaler* sc, uint16_t* out_slot, int64_t n, const DeviceWorkspace* ws) {
+    const int64_t t_new = st->t + 1;
+    const int cur = st->cur;
+    a->p_in = st->p[cur];
+    a->m_in = st->m[cur];
+    a->v_in = st->v[cur];
+    a->p_out = pingpong ? st->p[1 - cur] : st->p[0];
+    a->m_out = pingpong ? st->m[1 - cur] : st->m[0];
+    a->v_out = pingpong ? st->v[1 - cur] : st->v[0];
+    a->out16 = out_slot;
+    a->n = n;
+    a->inv_scale = 1.0f / sc->scale;
+    a->lr = hp->lr;
+    a->beta1 = hp->beta1;
+    a->beta2 = hp->beta2;
+    a->one_minus_beta1 = 1.0f - hp->beta1;
+    a->one_minus_beta2 = 1.0f - hp->beta2;
+    a->bias_corr1 = float(1.0 - std::pow(double(hp->beta1), double(t_new)));
+    a->bias_corr2 = float(1.0 - std::pow(double(hp->beta2), double(t_new)));
+    a->eps = hp->eps;
+    a->weight_decay = hp->weight_decay;
+    a->flag = ws->d_flag;
+    a->epoch = ws->epoch;
+    a->done = reinterpret_cast<unsigned long long*>(ws->d_flag + 16);
+    a->host_word = ws->h_word_dev;
+}
+
+// Commit or skip, and the loss scale.
+void commit_step(zero_shard_state* st, bool pingpong, zero_loss_scaler* sc, int32_t flag) {
+    if (flag) {
+        float ns = sc->scale * sc->backoff;
+        if (ns < sc->min_scale) ns = sc->min_scale;
+        sc->scale = ns;
+        sc->good_steps = 0;
+    } else {
+        st->t += 1;
+        if (pingpong) st->cur = 1 - st->cur;
+        sc->good_steps += 1;
+        if (sc->growth_interval > 0 && sc->good_steps >= sc->growth_interval) {
+            const float ns = sc->scale * sc->growth;
+            if (std::isfinite(ns)) sc->scale = ns;   // never grow into inf
+            sc->good_steps = 0;
+        }
+    }
+}
+
 }  // namespace
 }  // namespace zp
 
@@ -236,29 +360,11 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
                                uint16_t* out_slot, void* stream, int32_t* overflow) {
     zp::clear_error();
     if (!st || !hp || !sc) return fail(ZERO_ERR_INVALID_ARG, "zero_shard_step: NULL state, hparams or scaler");
-    const int64_t S = st->shard_elems;
-    if (S < 0) return fail(ZERO_ERR_INVALID_ARG, "shard_elems < 0");
-    if (S > std::numeric_limits<int64_t>::max() / 16) return fail(ZERO_ERR_INDEX_OVERFLOW, "shard too large");
     if (R < 1 || R > zp::kMaxContrib) return fail(ZERO_ERR_INVALID_ARG, "R must be in 1..16");
-    if (st->cur != 0 && st->cur != 1) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 or 1");
-    if (st->t < 0 || st->t == std::numeric_limits<int64_t>::max())
-        return fail(ZERO_ERR_INVALID_ARG, "step count out of range");
-    const bool has1[3] = {st->p[1] != nullptr, st->m[1] != nullptr, st->v[1] != nullptr};
-    const bool pingpong = has1[0];
-    if (has1[1] != pingpong || has1[2] != pingpong)
-        return fail(ZERO_ERR_INVALID_ARG, "p[1], m[1], v[1] must be all set or all NULL");
-    if (!pingpong && st->cur != 0) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 in place");
-    if (!std::isfinite(sc->scale) || !(sc->scale > 0.0f))
-        return fail(ZERO_ERR_INVALID_ARG, "loss scale must be finite and > 0");
-    if (!zp::finite_f(sc->backoff) || !(sc->backoff > 0.0f) || !zp::finite_f(sc->growth) ||
-        !(sc->growth > 0.0f) || !zp::finite_f(sc->min_scale) || sc->min_scale < 0.0f ||
-        sc->growth_interval < 0 || sc->good_steps < 0)
-        return fail(ZERO_ERR_INVALID_ARG, "invalid loss-scaler settings");
-    if (!zp::finite_f(hp->lr) || !zp::finite_f(hp->eps) || !(hp->eps > 0.0f) ||
-        !zp::finite_f(hp->weight_decay) ||
-        !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(ZERO_ERR_INVALID_ARG,
-                    "invalid Adam hyper-parameters (finite; eps > 0; betas in [0, 1))");
+    bool pingpong = false;
+    int rc = zp::check_step_scalars(st, hp, sc, &pingpong);
+    if (rc != ZERO_OK) return rc;
+    const int64_t S = st->shard_elems;
 
     if (S > 0) {
         if (!grads) return fail(ZERO_ERR_INVALID_ARG, "grads is NULL");
@@ -266,26 +372,10 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
             if (!grads[r]) return fail(ZERO_ERR_INVALID_ARG, "a gradient pointer is NULL");
             if (!zp::aligned(grads[r], 16)) return fail(ZERO_ERR_ALIGNMENT, "gradient not 16-byte aligned");
         }
-        const int sets = pingpong ? 2 : 1;
         zp::Range rs[7];
         int nr = 0;
-        for (int k = 0; k < sets; ++k) {
-            const float* arr[3] = {st->p[k], st->m[k], st->v[k]};
-            for (const float* a : arr) {
-                if (!a) return fail(ZERO_ERR_INVALID_ARG, "a state pointer is NULL");
-                if (!zp::aligned(a, 16)) return fail(ZERO_ERR_ALIGNMENT, "state array not 16-byte aligned");
-                const uintptr_t lo = reinterpret_cast<uintptr_t>(a);
-                rs[nr++] = {lo, lo + uintptr_t(S) * 4};
-            }
-        }
-        if (!out_slot) return fail(ZERO_ERR_INVALID_ARG, "out_slot is NULL");
-        if (!zp::aligned(out_slot, 2)) return fail(ZERO_ERR_ALIGNMENT, "out_slot not 2-byte aligned");
-        const uintptr_t olo = reinterpret_cast<uintptr_t>(out_slot);
-        rs[nr++] = {olo, olo + uintptr_t(S) * 2};
-        for (int i = 0; i < nr; ++i)
-            for (int j = i + 1; j < nr; ++j)
-                if (zp::overlap(rs[i], rs[j]))
-                    return fail(ZERO_ERR_INVALID_ARG, "state arrays and slot must not overlap");
+        rc = zp::check_state_arrays(st, pingpong, out_slot, S, rs, &nr);
+        if (rc != ZERO_OK) return rc;
         for (int r = 0; r < R; ++r) {
             const uintptr_t lo = reinterpret_cast<uintptr_t>(grads[r]);
             const zp::Range g = {lo, lo + uintptr_t(S) * 2};
@@ -297,55 +387,20 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
 
     int32_t flag = 0;
     if (S > 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
-        int rc = zp::check_stream_device(stream, dev, "zero_shard_step");
-        if (rc != ZERO_OK) return rc;
         zp::DeviceWorkspace* ws = nullptr;
-        rc = zp::get_workspace(dev, &ws);
+        std::unique_lock<std::mutex> lock;
+        int dev = 0;
+        rc = zp::begin_step(stream, "zero_shard_step", &ws, &lock, &dev);
         if (rc != ZERO_OK) return rc;
-        std::lock_guard<std::mutex> lock(ws->mu);
         hipStream_t s = static_cast<hipStream_t>(stream);
 
-        if (++ws->epoch == 0) {   // the flag words hold epochs; restart after wrap-around
-            e = hipMemsetAsync(ws->d_flag, 0, sizeof(uint32_t), s);
-            if (e != hipSuccess) return zp::fail_hip(e, "hipMemsetAsync (flag)");
-            __atomic_store_n(ws->h_word, 0ull, __ATOMIC_RELEASE);
-            ws->epoch = 1;
-        }
-
-        // Adam constants for step t + 1 (used only if the step is taken)
-        const int64_t t_new = st->t + 1;
         zp::StepLaunch a;
         std::memset(&a, 0, sizeof(a));
         for (int r = 0; r < R; ++r) a.grad[r] = grads[r];
         a.R = R;
-        const int cur = st->cur;
-        a.p_in = st->p[cur];
-        a.m_in = st->m[cur];
-        a.v_in = st->v[cur];
-        a.p_out = pingpong ? st->p[1 - cur] : st->p[0];
-        a.m_out = pingpong ? st->m[1 - cur] : st->m[0];
-        a.v_out = pingpong ? st->v[1 - cur] : st->v[0];
-        a.out16 = out_slot;
-        a.n = S;
-        a.inv_scale = 1.0f / sc->scale;
-        a.lr = hp->lr;
-        a.beta1 = hp->beta1;
-        a.beta2 = hp->beta2;
-        a.one_minus_beta1 = 1.0f - hp->beta1;
-        a.one_minus_beta2 = 1.0f - hp->beta2;
-        a.bias_corr1 = float(1.0 - std::pow(double(hp->beta1), double(t_new)));
-        a.bias_corr2 = float(1.0 - std::pow(double(hp->beta2), double(t_new)));
-        a.eps = hp->eps;
-        a.weight_decay = hp->weight_decay;
-        a.flag = ws->d_flag;
-        a.epoch = ws->epoch;
-        a.done = reinterpret_cast<unsigned long long*>(ws->d_flag + 16);
-        a.host_word = ws->h_word_dev;
+        zp::step_constants(&a, st, pingpong, hp, sc, out_slot, S, ws);
 
-        e = zp::timing_begin(s);
+        hipError_t e = zp::timing_begin(s);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
         if (pingpong) {
             e = zp::launch_fused_step(a, ws->cu_count, s);
@@ -369,29 +424,78 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
 
         if (flag && pingpong) {
             // the pass wrote the slot speculatively; restore fp16(master)
-            zp::StepLaunch r = a;
-            r.p_in = st->p[cur];
-            e = zp::launch_slot_from_master(r, ws->cu_count, s);
+            e = zp::launch_slot_from_master(a, ws->cu_count, s);
             if (e != hipSuccess) return zp::fail_hip(e, "slot restore kernel launch");
         }
     }
 
-    // commit or skip, and the loss scale
-    if (flag) {
-        float ns = sc->scale * sc->backoff;
-        if (ns < sc->min_scale) ns = sc->min_scale;
-        sc->scale = ns;
-        sc->good_steps = 0;
-    } else {
-        st->t += 1;
-        if (pingpong) st->cur = 1 - st->cur;
-        sc->good_steps += 1;
-        if (sc->growth_interval > 0 && sc->good_steps >= sc->growth_interval) {
-            const float ns = sc->scale * sc->growth;
-            if (std::isfinite(ns)) sc->scale = ns;   // never grow into inf
-            sc->good_steps = 0;
+    zp::commit_step(st, pingpong, sc, flag);
+    if (overflow) *overflow = flag;
+    return ZERO_OK;
+}
+
+extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_shard_state* st,
+                               const zero_adam_hparams* hp, zero_loss_scaler* sc,
+                               uint16_t* out_slot, void* stream, int32_t* overflow) {
+    zp::clear_error();
+    if (!layout || !st || !hp || !sc)
+        return fail(ZERO_ERR_INVALID_ARG, "zero_owner_step: NULL layout, state, hparams or scaler");
+    bool pingpong = false;
+    int rc = zp::check_step_scalars(st, hp, sc, &pingpong);
+    if (rc != ZERO_OK) return rc;
+    if (!pingpong) return fail(ZERO_ERR_INVALID_ARG, "the owner step needs ping-pong state (p[1], m[1], v[1])");
+    zp::OwnerLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    int bound_dev = -1;
+    rc = zp::owner_tables(layout, rank, &a, &bound_dev);
+    if (rc != ZERO_OK) return rc;
+    zero_layout_info info;
+    rc = zero_layout_get_info(layout, &info);
+    if (rc != ZERO_OK) return rc;
+    if (st->shard_elems != info.shard_elems)
+        return fail(ZERO_ERR_INVALID_ARG, "shard_elems differs from the layout's shard size");
+    const int64_t n = a.g_hi - a.g_lo;   // real elements of the rank's shard
+
+    if (n > 0) {
+        zp::Range rs[7];
+        int nr = 0;
+        rc = zp::check_state_arrays(st, pingpong, out_slot, n, rs, &nr);
+        if (rc != ZERO_OK) return rc;
+        for (int i = 0; i < nr; ++i)
+            if (zp::contributions_overlap(layout, rs[i].lo, rs[i].hi))
+                return fail(ZERO_ERR_INVALID_ARG, "a contribution tensor overlaps the state or the slot");
+    }
+
+    int32_t flag = 0;
+    if (n > 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+        if (dev != bound_dev) return fail(ZERO_ERR_STATE, "contributions were bound on another device");
+        zp::DeviceWorkspace* ws = nullptr;
+        std::unique_lock<std::mutex> lock;
+        rc = zp::begin_step(stream, "zero_owner_step", &ws, &lock, &dev);
+        if (rc != ZERO_OK) return rc;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, n, ws);
+        a.st.R = a.R;
+
+        e = zp::timing_begin(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+        e = zp::launch_owner_step(a, s);
+        if (e != hipSuccess) return zp::fail_hip(e, "owner step kernel launch");
+        e = zp::timing_end(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+        rc = zp::wait_for_flag(ws, s, ws->epoch, &flag);
+        if (rc != ZERO_OK) return rc;
+        if (flag) {
+            // the pass wrote the slot speculatively; restore fp16(master)
+            e = zp::launch_slot_from_master(a.st, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "slot restore kernel launch");
         }
     }
+
+    zp::commit_step(st, pingpong, sc, flag);
     if (overflow) *overflow = flag;
     return ZERO_OK;
 }

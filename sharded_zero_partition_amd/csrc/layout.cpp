@@ -17,6 +17,7 @@
 #include <limits>
 #include <mutex>
 #include <new>
+#include <utility>
 
 #include "zp_internal.hpp"
 
@@ -48,6 +49,9 @@ struct zero_layout {
     int64_t* d_rlen = nullptr;
     const uint16_t** d_rptr = nullptr;
     int32_t* d_rfirst = nullptr;
+    // host copy of the contribution tensors' byte ranges, sorted by start,
+    // with the running maximum of their ends (overlap queries)
+    std::vector<uintptr_t> r_start, r_end_max;
 };
 
 namespace {
@@ -77,6 +81,8 @@ void free_reduce_tables(zero_layout* l) {
     l->r_device = -1;
     l->r_ranks = 0;
     l->r_nsrc = 0;
+    l->r_start.clear();
+    l->r_end_max.clear();
 }
 
 // Chunk index over the flat stream: first[c] = index (among the non-empty
@@ -481,6 +487,26 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
     if (!chunk_index(offs, l->psi, &shift, &first))
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    std::vector<uintptr_t> starts, end_max;
+    try {
+        std::vector<std::pair<uintptr_t, uintptr_t>> rg;
+        rg.reserve(ptrs.size());
+        for (size_t k = 0; k < ptrs.size(); ++k) {
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(ptrs[k]);
+            rg.push_back({lo, lo + uintptr_t(lens[k % lens.size()]) * 2});
+        }
+        std::sort(rg.begin(), rg.end());
+        starts.reserve(rg.size());
+        end_max.reserve(rg.size());
+        uintptr_t m = 0;
+        for (const auto& r : rg) {
+            m = std::max(m, r.second);
+            starts.push_back(r.first);
+            end_max.push_back(m);
+        }
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -514,8 +540,44 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     l->r_nsrc = int32_t(offs.size());
     l->r_shift = shift;
     l->r_device = dev;
+    l->r_start.swap(starts);
+    l->r_end_max.swap(end_max);
     return ZERO_OK;
 }
+
+namespace zp {
+
+int owner_tables(const zero_layout* l, int32_t rank, ReduceLaunch* out, int* bound_dev) {
+    if (l->bucket <= 0) return fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (l->r_device < 0)
+        return fail(ZERO_ERR_STATE, "contributions not bound (zero_layout_bind_contributions)");
+    if (rank < 0 || rank >= l->n_ranks) return fail(ZERO_ERR_INVALID_ARG, "rank out of range");
+    *bound_dev = l->r_device;
+    const int64_t lo = int64_t(rank) * l->shard;
+    ReduceLaunch a;
+    a.off = l->d_roff;
+    a.len = l->d_rlen;
+    a.ptr = l->d_rptr;
+    a.first = l->d_rfirst;
+    a.n_src = l->r_nsrc;
+    a.chunk_shift = l->r_shift;
+    a.R = l->r_ranks;
+    a.base = lo;
+    a.g_lo = lo;
+    a.g_hi = std::max(lo, std::min(lo + l->shard, l->psi));
+    a.shard = nullptr;
+    *out = a;
+    return ZERO_OK;
+}
+
+bool contributions_overlap(const zero_layout* l, uintptr_t lo, uintptr_t hi) {
+    // ranges starting before hi: the first k; one of them meets [lo, hi)
+    // exactly when the largest end among them exceeds lo
+    const size_t k = size_t(std::lower_bound(l->r_start.begin(), l->r_start.end(), hi) - l->r_start.begin());
+    return lo < hi && k > 0 && l->r_end_max[k - 1] > lo;
+}
+
+}  // namespace zp
 
 extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t rank,
                                     uint16_t* shard, void* stream, int64_t* written) {

@@ -1,4 +1,5 @@
-// reduce_owner.hip -- the owner's share of a bucketed gradient reduce, gfx950.
+// reduce_owner.hip -- the owner's share of a bucketed gradient reduce, and the
+// owner step that feeds that reduce straight into the shard update, gfx950.
 //
 // In Stage 2 (P_os+g) of the ZeRO explainer page ("ZeRO: Memory Optimizations
 // Toward Training Trillion Parameter Models", azimuth.plus) every rank ends up
@@ -23,6 +24,17 @@
 // contribution is read as aligned 16-byte blocks (funnel-shifted when
 // misaligned); vectors at the range ends or across tensor boundaries go
 // element by element.  HBM bytes per element: 2R read + 2 written.
+//
+// The owner step runs the same walk over the owner's whole real range and,
+// in place of the fp16 store, the shard step's arithmetic (adam.hpp): the
+// overflow check of each sum, Adam on the fp32 master, momentum and variance
+// (read set -> write set) and the fp16 slot.  The Stage 2 reduce of the
+// owner's partition and its Stage 1 update are then one pass, with no fp16
+// gradient shard in between.  HBM bytes per element: 2R + 12 read, 12 + 2
+// written.  A wave that saw a non-finite sum raises the flag word to the
+// call's epoch; a one-thread kernel afterwards hands the decision to the
+// host.
+#include "adam.hpp"
 #include "vec16.hpp"
 #include "zp_internal.hpp"
 
@@ -71,6 +83,191 @@ __device__ __forceinline__ u32x4 next_block(const u32x4 v[kU], int u, u32x4 extr
     return lane == 63 ? first_of_next : nxt;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// What happens to the fp32 sums.  A cooperative span (all 2 x 64 vectors of
+// the wave full and inside the range) ends in `span_pre` (loads the
+// epilogue needs, issued before the contributions' loads) and `span_done`
+// (the span's sums s[u][e] of shard positions j0 + 512 u + 8 lane + e).
+// Other waves finish vector by vector: `pre` and `vec` for the 8-element
+// vector at shard position jv, `elem` for a single element j.  `finish` is
+// reached by every lane of every wave that did work.
+
+// Reduce-to-owner: fp16 of the sum into the owner's fp16 gradient shard.
+struct ToShard {
+    using Launch = ReduceLaunch;
+    struct SpanPre {};
+    struct Pre {};
+    __device__ static int mis(const Launch& a) {
+        return int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
+    }
+    __device__ static void span_pre(const Launch&, int64_t, int, SpanPre&) {}
+    __device__ static void span_done(const Launch& a, int64_t j0, const float s[kU][8], const SpanPre&,
+                                     int lane, bool&) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            uint32_t o[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
+            __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
+                                        reinterpret_cast<u32x4*>(a.shard + j0 + 512 * u + 8 * lane));
+        }
+    }
+    __device__ static void pre(const Launch&, int64_t, Pre&) {}
+    __device__ static void vec(const Launch& a, int64_t jv, const float s[8], const Pre&, bool&) {
+        uint32_t o[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = f2h(s[2 * d]) | (f2h(s[2 * d + 1]) << 16);
+        *reinterpret_cast<u32x4*>(a.shard + jv) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    __device__ static void elem(const Launch& a, int64_t j, float s, bool&) {
+        a.shard[j] = uint16_t(f2h(s));
+    }
+    __device__ static void finish(const Launch&, bool) {}
+};
+
+// Owner step: the shard step's arithmetic on element j of the owner's shard
+// (ping-pong: read set *_in, write set *_out and the fp16 slot).
+//
+// In a cooperative span lane l holds the sums of elements 8 l .. 8 l + 7 of
+// each 512-element group, but an fp32 access with that mapping covers only
+// half of every 64-byte run it touches, and such non-temporal stores cost
+// about 1.5x their bytes in HBM writes (measured).  So the sums go through
+// LDS (16 KiB per block, each wave its own 4 KiB) and come back as 4
+// consecutive elements per lane, 256 q + 4 l .. + 3 for q = 0..3: every
+// fp32 load and store instruction then covers 1 KiB contiguously, and the
+// fp16 slot 512 bytes.
+struct ToAdam {
+    using Launch = OwnerLaunch;
+    struct SpanPre {
+        f32x4 p[4], m[4], v[4];
+    };
+    struct Pre {
+        f32x4 p[2], m[2], v[2];
+    };
+    __device__ static int mis(const Launch&) { return 0; }   // p, m, v are 16-byte aligned
+    __device__ static void span_pre(const Launch& a, int64_t j0, int lane, SpanPre& q) {
+        const StepLaunch& c = a.st;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t e = j0 + 256 * k + 4 * lane;
+            q.p[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c.p_in + e));
+            q.m[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c.m_in + e));
+            q.v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(c.v_in + e));
+        }
+    }
+    __device__ static void span_done(const Launch& a, int64_t j0, const float s[kU][8], const SpanPre& q,
+                                     int lane, bool& bad) {
+        static_assert(kU == 2, "the transpose below assumes two 512-element groups");
+        __shared__ f32x4 lds[kThreads / 64][256];
+        f32x4* mine = lds[threadIdx.x >> 6];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            mine[128 * u + 2 * lane] = f32x4{s[u][0], s[u][1], s[u][2], s[u][3]};
+            mine[128 * u + 2 * lane + 1] = f32x4{s[u][4], s[u][5], s[u][6], s[u][7]};
+        }
+        // only this wave touches its slice: LDS operations of one wave
+        // complete in order, the fences keep the compiler from reordering
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const StepLaunch& c = a.st;
+        const uintptr_t slot_phase = reinterpret_cast<uintptr_t>(c.out16 + j0) & 7;   // wave-uniform
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 t = mine[64 * k + lane];
+            const float sk[4] = {t.x, t.y, t.z, t.w};
+            float p[4] = {q.p[k].x, q.p[k].y, q.p[k].z, q.p[k].w};
+            float m[4] = {q.m[k].x, q.m[k].y, q.m[k].z, q.m[k].w};
+            float v[4] = {q.v[k].x, q.v[k].y, q.v[k].z, q.v[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bad |= not_finite(sk[e]);
+                adam_element(c, sk[e], p[e], m[e], v[e]);
+            }
+            const int64_t e0 = j0 + 256 * k + 4 * lane;
+            __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, reinterpret_cast<f32x4*>(c.p_out + e0));
+            __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, reinterpret_cast<f32x4*>(c.m_out + e0));
+            __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(c.v_out + e0));
+            const uint32_t w0 = f2h(p[0]) | (f2h(p[1]) << 16);
+            const uint32_t w1 = f2h(p[2]) | (f2h(p[3]) << 16);
+            uint16_t* dst = c.out16 + e0;
+            if (slot_phase == 0) {
+                __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(dst));
+            } else if ((slot_phase & 3) == 0) {
+                __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(dst));
+                __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t*>(dst + 2));
+            } else {
+                dst[0] = uint16_t(w0);
+                dst[1] = uint16_t(w0 >> 16);
+                dst[2] = uint16_t(w1);
+                dst[3] = uint16_t(w1 >> 16);
+            }
+        }
+    }
+    // vector by vector (waves at the range ends or over tensor boundaries)
+    __device__ static void pre(const Launch& a, int64_t jv, Pre& q) {
+        const StepLaunch& c = a.st;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            q.p[h] = *reinterpret_cast<const f32x4*>(c.p_in + jv + 4 * h);
+            q.m[h] = *reinterpret_cast<const f32x4*>(c.m_in + jv + 4 * h);
+            q.v[h] = *reinterpret_cast<const f32x4*>(c.v_in + jv + 4 * h);
+        }
+    }
+    __device__ static void vec(const Launch& a, int64_t jv, const float s[8], const Pre& q, bool& bad) {
+        const StepLaunch& c = a.st;
+        float p[8] = {q.p[0].x, q.p[0].y, q.p[0].z, q.p[0].w, q.p[1].x, q.p[1].y, q.p[1].z, q.p[1].w};
+        float m[8] = {q.m[0].x, q.m[0].y, q.m[0].z, q.m[0].w, q.m[1].x, q.m[1].y, q.m[1].z, q.m[1].w};
+        float v[8] = {q.v[0].x, q.v[0].y, q.v[0].z, q.v[0].w, q.v[1].x, q.v[1].y, q.v[1].z, q.v[1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            bad |= not_finite(s[k]);
+            adam_element(c, s[k], p[k], m[k], v[k]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            *reinterpret_cast<f32x4*>(c.p_out + jv + 4 * h) = f32x4{p[4 * h], p[4 * h + 1], p[4 * h + 2], p[4 * h + 3]};
+            *reinterpret_cast<f32x4*>(c.m_out + jv + 4 * h) = f32x4{m[4 * h], m[4 * h + 1], m[4 * h + 2], m[4 * h + 3]};
+            *reinterpret_cast<f32x4*>(c.v_out + jv + 4 * h) = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+        }
+        // the slot may be only 2-byte aligned; jv is a multiple of 8, so every
+        // lane of the wave takes the same branch
+        uint32_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = f2h(p[2 * d]) | (f2h(p[2 * d + 1]) << 16);
+        uint16_t* dst = c.out16 + jv;
+        const uintptr_t x = reinterpret_cast<uintptr_t>(dst);
+        if ((x & 15) == 0) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        } else if ((x & 7) == 0) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+            *reinterpret_cast<u32x2*>(dst + 4) = u32x2{w[2], w[3]};
+        } else if ((x & 3) == 0) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) *reinterpret_cast<uint32_t*>(dst + 2 * d) = w[d];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    __device__ static void elem(const Launch& a, int64_t j, float s, bool& bad) {
+        const StepLaunch& c = a.st;
+        bad |= not_finite(s);
+        float p = c.p_in[j], m = c.m_in[j], v = c.v_in[j];
+        adam_element(c, s, p, m, v);
+        c.p_out[j] = p;
+        c.m_out[j] = m;
+        c.v_out[j] = v;
+        c.out16[j] = uint16_t(f2h(p));
+    }
+    __device__ static void finish(const Launch& a, bool bad) {
+        const unsigned long long ballot = __ballot(bad);
+        if (ballot != 0ull && (threadIdx.x & 63) == 0) atomicMax(a.st.flag, a.st.epoch);
+    }
+};
+
 // Cooperative span with a compile-time contribution count R.  The
 // contributions go in groups of up to kGroup: all of a group's kU aligned
 // blocks per lane (plus its extra blocks) are loaded before any is used, and
@@ -78,10 +275,13 @@ __device__ __forceinline__ u32x4 next_block(const u32x4 v[kU], int u, u32x4 extr
 // sixteen at once needs about 200 VGPRs and ran slower than two groups.)
 constexpr int kGroup = 4;
 
-template <int R>
-__device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_t rel0,
-                                          int64_t kw, int mis, int lane) {
+template <int R, class Epi>
+__device__ __forceinline__ void coop_span(const typename Epi::Launch& a, int src, int64_t rel0,
+                                          int64_t kw, int mis, int lane, bool& bad) {
     constexpr int G = R < kGroup ? R : kGroup;
+    const int64_t j0 = kw * 8 - mis;
+    typename Epi::SpanPre pre;
+    Epi::span_pre(a, j0, lane, pre);
     float s[kU][8];
     int64_t dep = 0;   // 0; makes a group's addresses wait for the previous group's sums
 #pragma unroll
@@ -121,24 +321,18 @@ __device__ __forceinline__ void coop_span(const ReduceLaunch& a, int src, int64_
         // stays 0 but is opaque to the compiler, and the next addresses add it.
         if (r0 + G < R) asm volatile("" : "+v"(dep) : "v"(s[0][0]));
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        uint32_t o[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = f2h(s[u][2 * d]) | (f2h(s[u][2 * d + 1]) << 16);
-        const int64_t jv = (kw + 64 * u + lane) * 8 - mis;
-        __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4*>(a.shard + jv));
-    }
+    Epi::span_done(a, j0, s, pre, lane, bad);
 }
 
-template <int R>
-__global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaunch a) {
+template <int R, class Epi>
+__device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     constexpr int nr = R;   // contributions (compile-time: every loop over them unrolls)
     const int lane = threadIdx.x & 63;
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wave_in_block;
     // vector k covers shard positions [8k - mis, 8k - mis + 8)
-    const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
+    const int mis = Epi::mis(a);
+    bool bad = false;
     const int64_t j_lo = a.g_lo - a.base;
     const int64_t j_hi = a.g_hi - a.base;
     const int64_t k_lo = (j_lo + mis) >> 3;
@@ -178,7 +372,8 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
         }
         if (in_bounds) {
             // every contribution's loads are issued before the first shuffle
-            coop_span<R>(a, lo, rel0, kw, mis, lane);
+            coop_span<R, Epi>(a, lo, rel0, kw, mis, lane, bad);
+            Epi::finish(a, bad);
             return;
         }
     }
@@ -195,6 +390,8 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
             const int64_t slen = one ? one_len : a.len[i];
             const int64_t rel = g0 - soff;
             if (rel + 8 <= slen) {
+                typename Epi::Pre pre;
+                Epi::pre(a, jv, pre);
                 float s[8];
                 int64_t dep = 0;   // as in coop_span: groups of kGroup contributions
 #pragma unroll
@@ -209,10 +406,7 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
                     }
                     if ((r + 1) % kGroup == 0 && r + 1 < nr) asm volatile("" : "+v"(dep) : "v"(s[0]));
                 }
-                uint32_t o[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) o[d] = f2h(s[2 * d]) | (f2h(s[2 * d + 1]) << 16);
-                *reinterpret_cast<u32x4*>(a.shard + jv) = u32x4{o[0], o[1], o[2], o[3]};
+                Epi::vec(a, jv, s, pre, bad);
                 continue;
             }
         }
@@ -224,22 +418,45 @@ __global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaun
             if (j < j_lo || j >= j_hi) continue;
             const int64_t g = a.base + j;
             const int i = search(a.off, lo, hi, g);
-            a.shard[j] = uint16_t(f2h(sum1<R>(a, i, g - a.off[i])));
+            Epi::elem(a, j, sum1<R>(a, i, g - a.off[i]), bad);
         }
     }
+    Epi::finish(a, bad);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void reduce_owner_kernel(const ReduceLaunch a) {
+    owner_body<R, ToShard>(a);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void owner_step_kernel(const OwnerLaunch a) {
+    owner_body<R, ToAdam>(a);
+}
+
+// One thread, launched after the owner step on its stream: copies the pass's
+// decision from the flag word into the pinned host word the host polls.
+__global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsigned long long* host_word) {
+    const uint32_t f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long word = (static_cast<unsigned long long>(epoch) << 1) | (f == epoch ? 1ull : 0ull);
+    __hip_atomic_store(host_word, word, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Workgroups for the vectors of shard positions [j_lo, j_hi) on a grid
+// shifted by mis elements.
+dim3 span_grid(int64_t j_lo, int64_t j_hi, int mis) {
+    const int64_t nvec = ((j_hi - 1 + mis) >> 3) + 1 - ((j_lo + mis) >> 3);
+    const int64_t waves = (nvec + kSpanVec - 1) / kSpanVec;
+    int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    if (blocks < 1) blocks = 1;
+    return dim3{unsigned(blocks)};
 }
 
 }  // namespace
 
 hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream) {
     const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
-    const int64_t j_lo = a.g_lo - a.base;
-    const int64_t j_hi = a.g_hi - a.base;
-    const int64_t nvec = ((j_hi - 1 + mis) >> 3) + 1 - ((j_lo + mis) >> 3);
-    const int64_t waves = (nvec + kSpanVec - 1) / kSpanVec;
-    int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
-    if (blocks < 1) blocks = 1;
-    const dim3 grid{unsigned(blocks)};
+    const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, mis);
     switch (a.R) {
         case 1: hipLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
         case 2: hipLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
@@ -258,6 +475,32 @@ hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream) {
         case 15: hipLaunchKernelGGL(reduce_owner_kernel<15>, grid, dim3(kThreads), 0, stream, a); break;
         default: hipLaunchKernelGGL(reduce_owner_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream) {
+    const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, 0);
+    switch (a.R) {
+        case 1: hipLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(owner_step_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(owner_step_kernel<3>, grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(owner_step_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL(owner_step_kernel<5>, grid, dim3(kThreads), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL(owner_step_kernel<6>, grid, dim3(kThreads), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL(owner_step_kernel<7>, grid, dim3(kThreads), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(owner_step_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+        case 9: hipLaunchKernelGGL(owner_step_kernel<9>, grid, dim3(kThreads), 0, stream, a); break;
+        case 10: hipLaunchKernelGGL(owner_step_kernel<10>, grid, dim3(kThreads), 0, stream, a); break;
+        case 11: hipLaunchKernelGGL(owner_step_kernel<11>, grid, dim3(kThreads), 0, stream, a); break;
+        case 12: hipLaunchKernelGGL(owner_step_kernel<12>, grid, dim3(kThreads), 0, stream, a); break;
+        case 13: hipLaunchKernelGGL(owner_step_kernel<13>, grid, dim3(kThreads), 0, stream, a); break;
+        case 14: hipLaunchKernelGGL(owner_step_kernel<14>, grid, dim3(kThreads), 0, stream, a); break;
+        case 15: hipLaunchKernelGGL(owner_step_kernel<15>, grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(owner_step_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(publish_flag_kernel, dim3(1), dim3(1), 0, stream, a.st.flag, a.st.epoch, a.st.host_word);
     return hipGetLastError();
 }
 

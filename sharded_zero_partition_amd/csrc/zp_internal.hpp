@@ -119,6 +119,32 @@ hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t
 // a skipped ping-pong step): out16[i] = fp16(p_in[i]).
 hipError_t launch_slot_from_master(const StepLaunch& a, int cu_count, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// owner step: the shard step fed straight from the R ranks' ragged tensors
+// ---------------------------------------------------------------------------
+
+// The reduce-to-owner tables and range (the `shard` member unused) plus the
+// shard step's state pointers and constants (its `grad` members unused).
+// Element j of the owner's shard is flat index base + j; the range
+// [g_lo, g_hi) is the owner's real elements.  p/m/v 16-byte aligned.
+struct OwnerLaunch : ReduceLaunch {
+    StepLaunch st;
+};
+
+// One pass over the range: reduce, Adam (reading set *_in, writing *_out) and
+// the fp16 slot; a wave that saw a non-finite sum raises st.flag to st.epoch.
+// A one-thread kernel after it writes (epoch << 1) | flag to st.host_word.
+hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream);
+
+// The reduce tables bound on `l` (layout.cpp) for an owner step of `rank`:
+// fills every ReduceLaunch member but `shard`, with [g_lo, g_hi) the rank's
+// real elements (empty when its shard is all padding), and the device the
+// tables live on.  Makes no HIP call.
+int owner_tables(const zero_layout* l, int32_t rank, ReduceLaunch* out, int* bound_dev);
+
+// True when the byte range [lo, hi) meets a bound contribution tensor of `l`.
+bool contributions_overlap(const zero_layout* l, uintptr_t lo, uintptr_t hi);
+
 // ZERO_OK when `stream` (NULL = the null stream) belongs to device `dev`,
 // else a STATE error naming `what`.
 int check_stream_device(void* stream, int dev, const char* what);

@@ -40,6 +40,7 @@ KIND_GRAD = 1
 KIND_SPECIAL = 2
 KIND_PACK = 3
 KIND_SIZES = 4
+KIND_STREAM = 5
 
 
 def gpt2_tensor_numels(n_layers: int, hidden: int, ffn: int, vocab: int,
@@ -266,3 +267,26 @@ def pack_sources(w: PackWorkload, device=None, views: bool = False, draw: int = 
         off += n
     del flat
     return out
+
+
+def gradient_stream(numels, wid: int, index: int, scale: float = 1.0, step: int = 1,
+                    device=None):
+    """Rank `index`'s whole fp16 gradient stream over the tensors `numels`:
+    fp16(float32(N(0, 1e-3)) * scale) bit patterns (torch.int16) in one
+    buffer, with a 0..7-element gap before each tensor so that every
+    alignment phase occurs.  Returns (buffer, starts, views): starts[i]
+    (numpy int64) is tensor i's first element in the buffer and views[i] the
+    tensor.  The gaps depend on the workload only, the values on (step,
+    index)."""
+    import torch
+    numels = [int(n) for n in numels]
+    gaps = host_rng(wid, KIND_STREAM, 0, 0).integers(0, 8, size=len(numels))
+    ends = np.cumsum(np.asarray(numels, np.int64) + gaps)
+    starts = ends - np.asarray(numels, np.int64)
+    n_buf = (int(ends[-1]) if numels else 0) + 8
+    t = normal_f32(n_buf, 1e-3, wid, KIND_STREAM, step, index, device)
+    t.mul_(np.float32(scale).item())
+    buf = t.to(torch.float16).view(torch.int16)
+    del t
+    views = [buf[int(s):int(s) + n] for s, n in zip(starts, numels)]
+    return buf, starts, views

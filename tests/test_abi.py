@@ -203,6 +203,37 @@ def test_reduce_to_owner_argument_errors_need_no_device(zp):
                                        ctypes.byref(n)) == -7                     # not bound
 
 
+def test_owner_step_argument_errors_need_no_device(zp):
+    """The owner step checks its layout, binding, state mode and scalars
+    before any HIP call, and modifies nothing when it refuses."""
+    lay = zp.partition_layout([10, 20], 4, bucket=16)         # S = 8, rank 3 holds padding only
+    hp = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    sc = zp.LossScaler.make(1024.0)
+    flag = ctypes.c_int32(-1)
+    base = 1 << 32
+    st = zp.ShardStateC()
+    st.shard_elems = 8
+    for k in range(2):
+        st.p[k], st.m[k], st.v[k] = base + 256 * (3 * k), base + 256 * (3 * k + 1), base + 256 * (3 * k + 2)
+    slot = ctypes.c_void_p(base + 4096)
+
+    def call(l=lay, rank=0, st=st, hp=hp, sc=sc, slot=slot):
+        return zp.lib.zero_owner_step(l._h if l is not None else None, rank, ctypes.byref(st),
+                                      ctypes.byref(hp), ctypes.byref(sc), slot, None, ctypes.byref(flag))
+    assert call() == -7                                                # contributions not bound
+    assert b"not bound" in zp.lib.zero_last_error()
+    assert call(l=zp.partition_layout([10, 20], 4)) == -7              # no bucket plan
+    assert call(l=None) == -1
+    inplace = zp.ShardStateC.from_buffer_copy(st)
+    inplace.p[1] = inplace.m[1] = inplace.v[1] = None
+    assert call(st=inplace) == -1
+    assert b"ping-pong" in zp.lib.zero_last_error()
+    assert call(hp=zp.AdamHParams(1e-4, 0.9, 0.999, 0.0, 0.0)) == -1   # eps must be > 0
+    # (binding uploads tables, so the rank, size and overlap checks that follow
+    # it are covered by the GPU tests)
+    assert sc.scale == 1024.0 and sc.good_steps == 0 and st.t == 0 and st.cur == 0
+
+
 def test_arena_plan_matches_oracle(zp):
     rng = random.Random(41)
     for _ in range(200):
