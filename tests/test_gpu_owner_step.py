@@ -35,8 +35,10 @@ class OwnerRun:
     """One owner's device ping-pong state, slot and scaler beside the
     oracle's.  Set 1 starts as NaN, so a read of it, or of padding, shows."""
 
-    def __init__(self, olay, rank: int, rng, scale=1024.0, slot_offset=3, slot_tail=5):
+    def __init__(self, olay, rank: int, rng, scale=1024.0, slot_offset=3, slot_tail=5, hp=HP):
         self.olay = olay
+        self.hp = hp
+        self.hpc = zp.AdamHParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)
         S, n = olay.shard, _real(olay, rank)
         self.S, self.n = S, n
         p0 = (rng.standard_normal(S, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
@@ -56,9 +58,9 @@ class OwnerRun:
         self.pad0 = [x[n:].clone() for x in (self.state.p, self.state.m, self.state.v)]
 
     def step(self, lay, rank, host_lists):
-        flag = lay.owner_step(rank, self.state, HPC, self.scaler, self.slot)
+        flag = lay.owner_step(rank, self.state, self.hpc, self.scaler, self.slot)
         torch.cuda.synchronize()
-        oflag = oracle.owner_step(host_lists, self.olay, rank, self.ostate, self.oscaler, HP, self.out16)
+        oflag = oracle.owner_step(host_lists, self.olay, rank, self.ostate, self.oscaler, self.hp, self.out16)
         assert flag == oflag, f"flag {flag} != oracle {oflag}"
         assert self.state.t == self.ostate.t
         assert self.scaler.scale == self.oscaler.scale
@@ -140,6 +142,42 @@ def test_small_ragged_layouts_every_rank(R):
                 assert run.step(lay, r, host) == 0
                 assert run.state.cur == (step + 1) % 2
             _redraw(rng, bufs)
+        lay.close()
+
+
+def test_seeded_random_cases():
+    """Random tensor lists, rank counts, alignments, R, loss scales and
+    hyper-parameters; one to three steps per case with new gradients, and
+    now and then an inf or NaN planted at a random flat index."""
+    rng = np.random.default_rng(2025)
+    for case in range(25):
+        numels = [int(x) for x in rng.choice([0, 1, 3, 8, 15, 64, 1000, 1024, 1025, 4097, 20000],
+                                             size=int(rng.integers(1, 30)))]
+        if sum(numels) == 0:
+            numels.append(5)
+        n_ranks = int(rng.integers(1, 9))
+        align = int(rng.choice([1, 8, 64]))
+        R = int(rng.integers(1, 17))
+        scale = float(2.0 ** rng.integers(0, 17))
+        hp = oracle.AdamHP(lr=float(rng.choice([1e-4, 1e-3, 3e-2])), beta1=float(rng.choice([0.0, 0.9])),
+                           beta2=float(rng.choice([0.99, 0.999])), eps=float(rng.choice([1e-8, 1e-6])),
+                           weight_decay=float(rng.choice([0.0, 0.05])))
+        lay = zp.partition_layout(numels, n_ranks, stage=2, align=align, bucket=1 << 12)
+        olay = OL.partition_layout(numels, n_ranks, 2, align, 1 << 12)
+        std = float(rng.choice([1e-4, 1e-3, 1e-2]))
+        bufs, lists = _lists(rng, numels, R, scale=scale * std / 1e-3)
+        lay.bind_contributions(lists)
+        rank = int(rng.integers(0, n_ranks))
+        run = OwnerRun(olay, rank, rng, scale=scale, slot_offset=int(rng.integers(0, 8)), hp=hp)
+        offs = np.concatenate([[0], np.cumsum(numels)])
+        for step in range(int(rng.integers(1, 4))):
+            if rng.random() < 0.25:
+                g = int(rng.integers(0, olay.psi))
+                i = int(np.searchsorted(offs, g, side="right") - 1)
+                bits = int(np.array(rng.choice([0x7C00, 0xFC00, 0x7E01]), np.uint16).view(np.int16))
+                lists[int(rng.integers(0, R))][i][g - int(offs[i])] = bits
+            run.step(lay, rank, _host(lists))
+            _redraw(rng, bufs, scale=scale * std / 1e-3)
         lay.close()
 
 
