@@ -25,7 +25,8 @@
  *   - "device" pointers point into GPU memory of the current HIP device;
  *     "host" pointers into ordinary host memory.  The caller owns every
  *     buffer it passes; the library keeps no pointer beyond the call except
- *     the tensor table given to zero_layout_bind_tensors.
+ *     the tensor tables given to zero_layout_bind_tensors and
+ *     zero_layout_bind_contributions.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is ordered on that stream, which must belong to the
  *     current device (a stream of another device is a STATE error).
@@ -357,9 +358,10 @@ int zero_owner_step(const zero_layout* layout, int32_t rank, zero_shard_state* s
 /* ------------------------------------------------------------------------ */
 
 /* Per calling thread.  While enabled (enable != 0), zero_shard_step,
- * zero_pack_bucket and zero_reduce_to_owner record a HIP event before their
- * first and after their last device kernel on the call's stream (for
- * zero_shard_step: the fused pass, or the check and update passes in place).
+ * zero_owner_step, zero_pack_bucket and zero_reduce_to_owner record a HIP
+ * event before their first and after their last device kernel on the call's
+ * stream (for zero_shard_step: the fused pass, or the check and update passes
+ * in place; for zero_owner_step: the pass and the flag hand-over).
  * The pairs go into a ring of 4096 per thread, so calls can be timed back to
  * back without waiting on the events; enabling or disabling clears it.
  * zero_last_kernel_ms waits for the most recent pair's end event and returns
