@@ -280,7 +280,7 @@ typedef struct zero_adam_hparams {
 
 /* Dynamic loss scale.  A step is skipped when any reduced gradient value is
  * inf or NaN: then scale = max(scale * backoff, min_scale), good_steps = 0
- * and no state changes.  A taken step increments good_steps, and when it
+ * and no state changes.  A taken step increments good_steps (saturating at INT32_MAX), and when it
  * reaches growth_interval (> 0) the scale is multiplied by growth and
  * good_steps reset. */
 typedef struct zero_loss_scaler {

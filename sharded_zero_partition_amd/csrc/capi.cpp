@@ -341,7 +341,7 @@ void commit_step(zero_shard_state* st, bool pingpong, zero_loss_scaler* sc, int3
     } else {
         st->t += 1;
         if (pingpong) st->cur = 1 - st->cur;
-        sc->good_steps += 1;
+        if (sc->good_steps < std::numeric_limits<int32_t>::max()) sc->good_steps += 1;   // saturates
         if (sc->growth_interval > 0 && sc->good_steps >= sc->growth_interval) {
             const float ns = sc->scale * sc->growth;
             if (std::isfinite(ns)) sc->scale = ns;   // never grow into inf

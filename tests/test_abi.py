@@ -234,6 +234,25 @@ def test_owner_step_argument_errors_need_no_device(zp):
     assert sc.scale == 1024.0 and sc.good_steps == 0 and st.t == 0 and st.cur == 0
 
 
+def test_good_step_count_saturates_without_a_device(zp):
+    """A shard step over an empty shard launches nothing, so the loss-scale
+    bookkeeping of a taken step runs on the CPU: with growth disabled the
+    good-step count saturates at INT32_MAX instead of overflowing."""
+    st = zp.ShardStateC()
+    st.shard_elems = 0
+    hp = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    sc = zp.LossScaler.make(1024.0)
+    sc.growth_interval = 0
+    sc.good_steps = 2 ** 31 - 2
+    flag = ctypes.c_int32(-1)
+    grads = (ctypes.c_void_p * 1)(None)
+    for _ in range(2):
+        assert zp.lib.zero_shard_step(ctypes.byref(st), grads, 1, ctypes.byref(hp), ctypes.byref(sc),
+                                      None, None, ctypes.byref(flag)) == 0
+        assert flag.value == 0 and sc.good_steps == 2 ** 31 - 1 and sc.scale == 1024.0
+    assert st.t == 2
+
+
 def test_arena_plan_matches_oracle(zp):
     rng = random.Random(41)
     for _ in range(200):
