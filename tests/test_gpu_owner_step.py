@@ -181,6 +181,35 @@ def test_seeded_random_cases():
         lay.close()
 
 
+def test_every_finite_fp16_class():
+    """Contributions drawn as random fp16 bit patterns with a finite
+    exponent: subnormals, signed zeros and values up to 65504 (16 of them sum
+    to a finite fp32 value, so no step is skipped)."""
+    rng = np.random.default_rng(31)
+    numels = [int(x) for x in rng.integers(1, 5000, size=30)]
+    for R in (2, 5, 16):
+        lay = zp.partition_layout(numels, 3, stage=2, bucket=1 << 12)
+        olay = OL.partition_layout(numels, 3, 2, 1, 1 << 12)
+        lists = []
+        for _ in range(R):
+            gaps = rng.integers(0, 9, size=len(numels))
+            bits = rng.integers(0, 1 << 16, size=int(sum(numels) + gaps.sum() + 8), dtype=np.uint16)
+            bits[(bits & 0x7C00) == 0x7C00] &= 0xBFFF            # inf/NaN exponent -> finite
+            buf = torch.from_numpy(bits.view(np.int16)).cuda()
+            lst, off = [], 0
+            for n, g in zip(numels, gaps):
+                off += int(g)
+                lst.append(buf[off:off + n])
+                off += n
+            lists.append(lst)
+        lay.bind_contributions(lists)
+        host = _host(lists)
+        for r in range(3):
+            run = OwnerRun(olay, r, rng, scale=65536.0)
+            assert run.step(lay, r, host) == 0
+        lay.close()
+
+
 @pytest.mark.parametrize("value", [np.inf, -np.inf, np.nan])
 def test_special_values_inside_and_outside_the_range(value):
     rng = np.random.default_rng(7)
