@@ -51,29 +51,31 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def load(path: str):
+    """Open a compiled copy of zero_oracle.c and declare its signatures."""
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.zo_half_to_float.argtypes = [ctypes.c_uint16]
+    L.zo_half_to_float.restype = f32
+    L.zo_float_to_half.argtypes = [f32]
+    L.zo_float_to_half.restype = ctypes.c_uint16
+    L.zo_half_to_float_n.argtypes = [P, P, i64]
+    L.zo_float_to_half_n.argtypes = [P, P, i64]
+    L.zo_reduce.argtypes = [P, i32, P, i64]
+    L.zo_overflow_flag.argtypes = [P, i32, i64]
+    L.zo_overflow_flag.restype = i32
+    L.zo_adam_apply.argtypes = [P, i32, P, P, P, P, i64, f32, i64,
+                                f32, f32, f32, f32, f32]
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        i64, i32, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_float
-        L.zo_half_to_float.argtypes = [ctypes.c_uint16]
-        L.zo_half_to_float.restype = f32
-        L.zo_float_to_half.argtypes = [f32]
-        L.zo_float_to_half.restype = ctypes.c_uint16
-        L.zo_half_to_float_n.argtypes = [P, P, i64]
-        L.zo_float_to_half_n.argtypes = [P, P, i64]
-        L.zo_reduce.argtypes = [P, i32, P, i64]
-        L.zo_overflow_flag.argtypes = [P, i32, i64]
-        L.zo_overflow_flag.restype = i32
-        L.zo_adam_apply.argtypes = [P, i32, P, P, P, P, i64, f32, i64,
-                                    f32, f32, f32, f32, f32]
-        L.zo_shard_step.argtypes = [P, i32, P, P, P, P, i64, f32, i64,
-                                    f32, f32, f32, f32, f32]
-        L.zo_shard_step.restype = i32
-        _lib = L
+        _lib = load(_LIB)
     return _lib
 
 

@@ -202,19 +202,3 @@ void zo_adam_apply(const uint16_t* const* contrib, int32_t R,
             out16[i] = zo_float_to_half(pi);
     }
 }
-
-/* One whole shard step for one rank: returns the overflow flag.  When the
- * flag is set nothing is written (the step is skipped); otherwise the state
- * is updated with step number t_before + 1. */
-int32_t zo_shard_step(const uint16_t* const* contrib, int32_t R,
-                      float* p, float* m, float* v, uint16_t* out16, int64_t n,
-                      float scale, int64_t t_before,
-                      float lr, float beta1, float beta2, float eps, float wd)
-{
-    int32_t flag = zo_overflow_flag(contrib, R, n);
-    if (flag)
-        return flag;
-    zo_adam_apply(contrib, R, p, m, v, out16, n, scale, t_before + 1,
-                  lr, beta1, beta2, eps, wd);
-    return 0;
-}

@@ -64,6 +64,8 @@ def test_first_step_closed_form():
     bound = 0.5 * _ulp32(st.p) + 4 * 2.0 ** -23 * np.abs(delta)
     assert (err <= bound).all(), float((err / bound).max())
     assert st.t == 1
+    # the fp16 slot is the new master rounded by numpy's float16 conversion
+    assert np.array_equal(out16, st.p.astype(np.float16).view(np.uint16))
     # the alternative reading (eps scaled by 1/sqrt(1-beta2) inside the step
     # size) differs far beyond the bound on the small-gradient elements
     alt = p0.astype(np.float64) - lr * g / (np.abs(g) + eps / np.sqrt(1 - float(F32(HP.beta2))))
@@ -172,6 +174,19 @@ def test_overflow_flag_brute_force_and_skip():
             assert (out16 == 0x5A5A).all() and st.t == 7 and sc.scale == 2048.0
         else:
             assert st.t == 8 and sc.scale == 4096.0 and not (out16 == 0x5A5A).all()
+
+
+def test_overflow_flag_at_the_ends():
+    """A single non-finite sum at the first or the last element, in the first
+    or the last contribution, raises the flag (brute force over the sums)."""
+    rng = np.random.default_rng(6)
+    for n in (1, 2, 17, 4096):
+        for where in {0, n - 1}:
+            for r in (0, 2):
+                c = _contribs(rng, n, 3, 1024.0)
+                assert oracle.overflow_flag(c) == 0
+                c[r][where] = 0x7E00
+                assert oracle.overflow_flag(c) == 1, (n, where, r)
 
 
 def test_inf_minus_inf_is_flagged():

@@ -63,6 +63,22 @@ def test_stage_closed_forms_exact_when_n_divides_psi():
         assert opt == 12 * psi // n      # optimizer states 12 Psi -> 12 Psi / N
 
 
+def test_replicated_states_are_the_unpadded_model():
+    """Plain data parallelism holds the whole model on every rank: 16 Psi
+    bytes for any N, whether or not N divides Psi; a replicated kind at a
+    later stage is the whole unpadded model (2 Psi), a partitioned one the
+    padded shard."""
+    for psi, n in ((10, 3), (1001, 8), (7, 64), (12345, 7)):
+        assert OL.stage_bytes_per_rank(psi, n, 0) == 16 * psi
+        for stage in (1, 2):
+            lay = OL.partition_layout([psi], n, stage=stage)
+            assert lay.padded > psi
+            assert lay.rank_bytes()["param16"] == 2 * psi
+        lay = OL.partition_layout([psi], n, stage=1)
+        assert lay.rank_bytes()["grad16"] == 2 * psi
+        assert lay.rank_bytes()["master"] == 4 * lay.shard
+
+
 def test_savings_on_64_gpus_round_to_page_figures():
     cases = {c["stage"]: c for c in _golden()["worked_examples"] if "n_ranks" in c and "psi" not in c}
     psi = 64 * 10 ** 6
