@@ -147,6 +147,14 @@ def zero3_1t() -> ShardWorkload:
                          special_step=2, special_fraction=1e-7)
 
 
+def past_2_31() -> ShardWorkload:
+    """Edge case, not one of the five workloads: a single rank's shard of
+    2^31 + 4099 elements, so element indices pass the signed 32-bit range and
+    the shard ends in a ragged tail; R = 1, scale 1024, 2 steps."""
+    return ShardWorkload("past_2_31", 9, [(1 << 31) + 4099], n_ranks=1, rank=0, n_contrib=1,
+                         scale=1024.0, steps=2, stage=3, gather_slots=1)
+
+
 SHARD_WORKLOADS = {w().name: w for w in (tiny, gpt2_1p5b, zero3_13b, zero3_1t)}
 
 

@@ -394,6 +394,17 @@ def test_13b_rank63_sampled():
     _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3)
 
 
+def test_shard_past_2_31_sampled():
+    """Element indices past the signed 32-bit range: rank 1 of 2 over three
+    tensors of 2^32 + 8198 elements in all, so its shard (2^31 + 4099
+    elements) starts past flat index 2^31, reaches past 2^32 and holds a
+    tensor boundary; R = 2 streams, two steps."""
+    numels = [(1 << 31) + 4096, (1 << 31) - 7, 4109]
+    torch.cuda.empty_cache()
+    _sampled_owner_steps(numels, 2, 1, 2, W.past_2_31().wid, 1024.0, 2, n_sample=1 << 18)
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("rank", [0, 15])
 def test_pack_20k_stream_sampled(rank):
     """The 20,000 log-uniform tensors (5.48e9 elements) cut for 16 owners:
