@@ -333,13 +333,16 @@ def test_errors():
 # full sizes, sampled
 # ---------------------------------------------------------------------------
 
-def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1 << 20):
+def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1 << 20, plant=None):
     """R whole gradient streams (workloads.gradient_stream), the owner step of
     `rank` for `steps` steps with new streams each step, compared on a sample
     of the rank's real elements (both range ends, every tensor boundary
     inside the range, and n_sample random positions) against the oracle's
-    shard step over the sampled sums; the overflow flag must be 0 (finite
-    inputs whose pairwise fp32 sums cannot overflow)."""
+    shard step over the sampled sums.  The draws are finite and their
+    pairwise fp32 sums cannot overflow, so the overflow flag is 0 unless
+    `plant` ({step: [(contribution, flat index, fp16 bits)]}) puts a special
+    value inside the rank's range on that step; planted positions inside the
+    range are part of the sample.  Returns the flags."""
     psi = int(sum(numels))
     lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=1 << 26)
     S = lay.info.shard_elems
@@ -348,8 +351,10 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     offs = np.concatenate([[0], np.cumsum(np.asarray(numels, np.int64))])
     rng = np.random.default_rng(wid * 100 + rank)
     inner = offs[(offs > lo) & (offs < lo + n)] - lo
+    planted = [g - lo for v in (plant or {}).values() for _, g, _ in v if lo <= g < lo + n]
     pick = np.concatenate([np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n),
-                           inner, inner - 1, rng.integers(0, n, size=n_sample)])
+                           inner, inner - 1, rng.integers(0, n, size=n_sample),
+                           np.asarray(planted, np.int64)])
     sample = np.unique(pick[(pick >= 0) & (pick < n)]).astype(np.int64)
     g = sample + lo
     tens = np.searchsorted(offs, g, side="right") - 1
@@ -364,18 +369,29 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     sc, osc = zp.LossScaler.make(scale), oracle.LossScaler(scale)
     print(f"[owner step] psi={psi} ranks={n_ranks} rank={rank} S={S} n={n} R={R} "
           f"sample={sample.size}", flush=True)
+    flags = []
+    out16 = np.empty(sample.size, np.uint16)
     for step in range(1, steps + 1):
-        streams = [W.gradient_stream(numels, wid, r, scale, step, "cuda") for r in range(R)]
+        streams = [W.gradient_stream(numels, wid, r, osc.scale, step, "cuda") for r in range(R)]
+        want_flag = 0
+        for r, g, bits in (plant or {}).get(step, []):
+            buf, starts, _ = streams[r]
+            ti = int(np.searchsorted(offs, g, side="right") - 1)
+            buf[int(starts[ti] + g - offs[ti])] = int(np.int16(np.uint16(bits)))
+            want_flag |= int(lo <= g < lo + n)
         lay.bind_contributions([views for _, _, views in streams])
         flag = lay.owner_step(rank, st, HPC, sc, slot)
         torch.cuda.synchronize()
-        assert flag == 0
+        assert flag == want_flag, f"step {step}: flag {flag}, expected {want_flag}"
+        flags.append(flag)
         contribs = []
         for buf, starts, _ in streams:
             pos = torch.from_numpy(starts[tens] + rel).cuda()
             contribs.append(buf[pos].cpu().numpy().view(np.uint16))
-        out16 = np.empty(sample.size, np.uint16)
-        oracle.shard_step(ost, contribs, osc, HP, out16, flag=0)
+        oracle.shard_step(ost, contribs, osc, HP, out16, flag=want_flag)
+        if want_flag:
+            # a skipped step restores the slot to fp16 of the live master
+            out16[:] = oracle.float_to_half(ost.p)
         del streams
         assert st.t == ost.t and sc.scale == osc.scale
         for name, got, want in zip("pmv", st.live(), (ost.p, ost.m, ost.v)):
@@ -384,6 +400,7 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
             assert bad.size == 0, f"step {step} {name}: {bad.size} differ, first at {sample[bad[0]]}"
         assert np.array_equal(slot[idx].cpu().numpy().view(np.uint16), out16), f"step {step} slot"
     lay.close()
+    return flags
 
 
 def test_13b_rank63_sampled():
@@ -392,6 +409,22 @@ def test_13b_rank63_sampled():
     loss scale 1024, three steps."""
     w = W.zero3_13b()
     _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3)
+
+
+def test_13b_rank63_overflow_sampled():
+    """The benchmark's owner-step configuration with an overflow: on step 2
+    contribution 1 holds +inf at a position inside rank 63's range and
+    contribution 0 a NaN outside it (rank 62's).  Flags 0, 1, 0; the skipped
+    step leaves the state as it was and restores the whole slot to fp16 of
+    the master; the loss scale halves and the next step runs at the new
+    scale.  Sampled against the oracle, the planted position included."""
+    w = W.zero3_13b()
+    S = -(-sum(w.numels) // w.n_ranks)
+    lo = w.rank * S
+    plant = {2: [(1, lo + 12_345_678, 0x7C00), (0, lo - 1000, 0x7E00)]}
+    flags = _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3,
+                                 n_sample=1 << 18, plant=plant)
+    assert flags == [0, 1, 0]
 
 
 def test_shard_past_2_31_sampled():
