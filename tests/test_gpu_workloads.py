@@ -1,8 +1,8 @@
 """GPU parity on the four shard-step workloads at their full sizes, in the
 launch configuration the benchmark times (single-pass ping-pong state), and
-in place for the small ones.  Every element is compared where the oracle
-finishes in seconds (tiny, GPT-2 1.5B); at 13B and 1T the oracle runs on a
-sample -- the first and last 8192 elements, one million random ones and every
+in place (overflow check pass, then the update pass).  Every element is
+compared where the oracle finishes in seconds (tiny, GPT-2 1.5B); at 13B and
+1T the oracle runs on a sample -- the first and last 8192 elements, one million random ones and every
 injected inf/NaN position -- which is exact because each element's update
 depends only on its own inputs and the global overflow decision."""
 
@@ -87,20 +87,22 @@ def test_gpt2_1p5b(pingpong):
     assert ls.bit_exact
 
 
-def test_zero3_13b():
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+def test_zero3_13b(pingpong):
     w = W.zero3_13b()
     assert w.shard == 200_752_240
-    ls = _run(w, True, sample=_sample(w.shard, seed=3))
+    ls = _run(w, pingpong, sample=_sample(w.shard, seed=3))
     assert ls.flags == [0] * 5 and ls.ts == [1, 2, 3, 4, 5]
     assert ls.bit_exact
 
 
-def test_zero3_1t_overflow_trace():
+@pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
+def test_zero3_1t_overflow_trace(pingpong):
     w = W.zero3_1t()
     assert w.shard == 976_562_500
     pos, vals = W.special_positions(w)
     assert len(pos) == 98
-    ls = _run(w, True, sample=_sample(w.shard, extra=pos, seed=5), full_flag=False)
+    ls = _run(w, pingpong, sample=_sample(w.shard, extra=pos, seed=5), full_flag=False)
     assert ls.flags == [0, 1, 0, 0, 0]
     assert ls.scales == [65536.0, 65536.0, 32768.0, 32768.0, 32768.0]
     assert ls.ts == [1, 1, 2, 3, 4]
