@@ -384,8 +384,17 @@ def test_arena_layout_invariants():
         lay = OL.partition_layout(numels, n_ranks, rng.randint(0, 3), align, bucket,
                                   with_segments=False)
         ab = rng.choice([256, 4096, 1 << 21])
-        plan, total = OL.arena_plan(lay, pingpong=rng.random() < 0.5, n_contrib=rng.randint(0, 4),
+        pp, nc = rng.random() < 0.5, rng.randint(0, 4)
+        plan, total = OL.arena_plan(lay, pingpong=pp, n_contrib=nc,
                                     with_bucket=bucket > 0 and rng.random() < 0.5, align_bytes=ab)
+        # the ping-pong set mirrors the fp32 state; each contribution is one
+        # fp16 shard
+        for k in ("master", "momentum", "variance"):
+            assert (k + "_alt" in plan) == pp
+            if pp:
+                assert plan[k + "_alt"][1] == plan[k][1]
+        for r in range(nc):
+            assert plan[f"contrib{r}"][1] == 2 * lay.shard
         spans = sorted(plan.values())
         for (o, b) in spans:
             assert o % ab == 0 and b >= 0

@@ -175,10 +175,21 @@ LAYOUT_MUTANTS = {
                                   "hi = min((fill + 1) * lay.bucket, (rank + 1) * lay.shard)", 1),
     "owner_range_ignores_fill": ("lo = max(fill * lay.bucket, rank * lay.shard)",
                                  "lo = rank * lay.shard", 1),
+    # contiguous arena (memory defragmentation paragraph)
+    "arena_params_partitioned_at_stage2": ('"param16": (S if st >= 3 else P, 2)',
+                                           '"param16": (S if st >= 2 else P, 2)', 1),
+    "arena_grads_partitioned_at_stage1": ('"grad16": (S if st >= 2 else P, 2)',
+                                          '"grad16": (S if st >= 1 else P, 2)', 1),
+    "arena_alternates_as_fp16": ('elems[k + "_alt"] = elems[k]',
+                                 'elems[k + "_alt"] = (elems[k][0], 2)', 1),
+    "arena_buffers_unaligned": ("off = -(-off // align_bytes) * align_bytes", "off = off", 1),
 }
 
 INIT_MUTANTS = {
     "backoff_grows_scale": ("np.float32(self.scale * self.backoff)", "np.float32(self.scale * self.growth)", 1),
+    "backoff_ignores_floor": ("max(float(np.float32(self.scale * self.backoff)), self.min_scale)",
+                              "float(np.float32(self.scale * self.backoff))", 1),
+    "scaler_never_sees_overflow": ("scaler.update(bool(flag))", "scaler.update(False)", 2),
     "skipped_step_still_updates": ("    if not flag:\n        adam_apply(contribs, state.p, state.m",
                                    "    if True:\n        adam_apply(contribs, state.p, state.m", 1),
     "skipped_step_advances_t": ("        state.t += 1\n    scaler.update(bool(flag))\n    return int(flag)\n\n\ndef reduce_to_owner",
