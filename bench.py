@@ -87,6 +87,8 @@ def parse_args():
                          "scale reference of the HBM counter runs)")
     ap.add_argument("--no-rank-iteration", action="store_true",
                     help="skip the 13B rank's full gradient-stream pack + step measurement")
+    ap.add_argument("--no-placement-spread", action="store_true",
+                    help="skip re-timing the step on re-allocated buffers")
     ap.add_argument("--no-owner-step", action="store_true",
                     help="skip the owner-step measurement (shard step fed from the ranks' tensor lists)")
     ap.add_argument("--pack-views", action="store_true",
@@ -329,6 +331,39 @@ def main():
     del step, st, grads, gather, slot, p0, arena
     torch.cuda.empty_cache()
 
+    # The same step on freshly allocated buffers placed behind padding
+    # allocations of several sizes: the kernel's time follows where its nine
+    # buffers land physically.  Reported beside `value`, which is the first
+    # measurement above and is never replaced by these.
+    placement = None
+    if not args.no_placement_spread:
+        spread = []
+        for pad_gb in (0, 7, 19, 31, 43):
+            torch.cuda.empty_cache()
+            pad = torch.empty(pad_gb << 30, dtype=torch.uint8, device=dev) if pad_gb else None
+            pp0 = W.master_init(w, device=dev)
+            pst = zp.ShardState(pp0, torch.zeros_like(pp0), torch.zeros_like(pp0),
+                                torch.empty_like(pp0), torch.empty_like(pp0), torch.empty_like(pp0))
+            pgr = [W.grad_contribution(w, 1, r, w.scale, device=dev) for r in range(R)]
+            pslot = torch.empty(S, dtype=torch.int16, device=dev)
+            pstep = zp.PreparedStep(pst, pgr, hp, zp.LossScaler.make(w.scale), pslot)
+            for _ in range(3):
+                pstep()
+            torch.cuda.synchronize()
+            zp.set_kernel_timing(True)
+            for _ in range(args.steps):
+                assert pstep() == 0
+            torch.cuda.synchronize()
+            spread.append(round(float(np.mean(zp.kernel_times())), 4))
+            zp.set_kernel_timing(False)
+            del pstep, pst, pgr, pslot, pp0, pad
+        torch.cuda.empty_cache()
+        placement = {"kernel_ms": spread, "padding_gb": [0, 7, 19, 31, 43],
+                     "frac": [round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) for ms in spread],
+                     "what": f"the same step re-timed ({args.steps} steps each) on freshly allocated "
+                             "buffers behind padding allocations of these sizes; value and roofline "
+                             "are the first measurement"}
+
     # NEXT: the owner step -- the same rank's shard step with its sum taken
     # straight from R = 2 ranks' whole gradient streams of the model (484
     # tensors each, one buffer per rank with 0..7-element gaps), so the
@@ -540,6 +575,7 @@ def main():
         "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
+        "placement_spread": placement,
         "library_copy": library_copy,
         "rank_iteration": rank_iteration,
         "layout_ms": round(layout_ms, 3),
