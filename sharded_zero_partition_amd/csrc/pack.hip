@@ -197,7 +197,8 @@ constexpr int kPackSpanU = 2;
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream) {
     constexpr int64_t kSpan = 512 * kPackSpanU;
     const int64_t waves = (a.bucket_elems + kSpan - 1) / kSpan;
-    int64_t blocks = (waves + 3) / 4;
+    constexpr int64_t kWavesPerBlock = kPackThreads / 64;
+    int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(pack_span_kernel<kPackSpanU>, dim3(unsigned(blocks)), dim3(kPackThreads), 0,
                        stream, a);
