@@ -316,7 +316,8 @@ template <bool kFlag, bool kSkip, int R>
 void launch_tiled_r(const StepLaunch& a, int cu_count, hipStream_t s) {
     constexpr int H = halves_for<R>();
     const int64_t ntiles = a.n / (256 * H);
-    int64_t blocks = (ntiles + 3) / 4;
+    constexpr int64_t kWavesPerBlock = kThreads / 64;
+    int64_t blocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * blocks_per_cu_tiled();
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;   // block 0 also owns the tail
