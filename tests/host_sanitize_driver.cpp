@@ -1,0 +1,249 @@
+// host_sanitize_driver.cpp -- the library's host code (layout.cpp, capi.cpp)
+// and the scalar C oracle, built with AddressSanitizer and
+// UndefinedBehaviorSanitizer and driven without a device.
+//
+// The kernel launch functions live in the .hip sources, which this build
+// leaves out: the stubs below stand in for them and fail if reached, since
+// nothing here may launch.  The driver exercises
+//   - partition layouts of seeded random tensor lists: info, offsets, rank
+//     ranges, all three segment queries with their sizing protocol, arena
+//     plans for every stage, with invariants checked on the way;
+//   - argument errors of every entry point that can be called without a
+//     device, with fake (never dereferenced) device addresses;
+//   - the oracle's conversions, reduce, flag and Adam on random data.
+// Any sanitizer report aborts with a non-zero exit status; the driver prints
+// "OK" at the end.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "zp_internal.hpp"
+
+namespace zp {
+static hipError_t never(const char* what) {
+    std::fprintf(stderr, "kernel launch reached in a host-only build: %s\n", what);
+    std::abort();
+}
+hipError_t launch_pack(const PackLaunch&, hipStream_t) { return never("pack"); }
+hipError_t launch_reduce_owner(const ReduceLaunch&, hipStream_t) { return never("reduce"); }
+hipError_t launch_fused_step(const StepLaunch&, int, hipStream_t) { return never("step"); }
+hipError_t launch_check(const StepLaunch&, int, hipStream_t) { return never("check"); }
+hipError_t launch_update_in_place(const StepLaunch&, int, hipStream_t) { return never("update"); }
+hipError_t launch_slot_from_master(const StepLaunch&, int, hipStream_t) { return never("slot"); }
+hipError_t launch_owner_step(const OwnerLaunch&, hipStream_t) { return never("owner"); }
+}  // namespace zp
+
+extern "C" {
+float zo_half_to_float(uint16_t h);
+uint16_t zo_float_to_half(float x);
+void zo_half_to_float_n(const uint16_t* in, float* out, int64_t n);
+void zo_float_to_half_n(const float* in, uint16_t* out, int64_t n);
+void zo_reduce(const uint16_t* const* contrib, int32_t R, float* sum_out, int64_t n);
+int32_t zo_overflow_flag(const uint16_t* const* contrib, int32_t R, int64_t n);
+void zo_adam_apply(const uint16_t* const* contrib, int32_t R, float* p, float* m, float* v,
+                   uint16_t* out16, int64_t n, float scale, int64_t t, float lr, float beta1,
+                   float beta2, float eps, float wd);
+}
+
+static uint64_t g_rng = 0x9E3779B97F4A7C15ull;
+static uint64_t next_u64() {   // xorshift64*
+    g_rng ^= g_rng >> 12;
+    g_rng ^= g_rng << 25;
+    g_rng ^= g_rng >> 27;
+    return g_rng * 0x2545F4914F6CDD1Dull;
+}
+static int64_t pick(const int64_t* v, int n) { return v[next_u64() % uint64_t(n)]; }
+
+static int g_fail = 0;
+#define CHECK(cond)                                                            \
+    do {                                                                       \
+        if (!(cond)) {                                                         \
+            std::fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #cond); \
+            g_fail = 1;                                                        \
+        }                                                                      \
+    } while (0)
+
+static void layouts() {
+    const int64_t sizes[] = {0, 1, 2, 3, 5, 8, 13, 40, 97, 300, 4096, 100003};
+    const int64_t aligns[] = {1, 2, 8, 64};
+    const int64_t buckets[] = {0, 0, 1, 7, 16, 100, 4096};
+    for (int trial = 0; trial < 300; ++trial) {
+        const int nt = int(next_u64() % 12);
+        std::vector<int64_t> numel(size_t(nt) + 1);
+        int64_t psi = 0;
+        for (int i = 0; i < nt; ++i) psi += (numel[size_t(i)] = pick(sizes, 12));
+        const int32_t N = int32_t(1 + next_u64() % 70);
+        const int32_t stage = int32_t(next_u64() % 4);
+        const int64_t A = pick(aligns, 4), B = pick(buckets, 7);
+        zero_layout* l = nullptr;
+        CHECK(zero_partition_layout(numel.data(), nt, N, stage, A, B, &l) == ZERO_OK);
+        if (!l) continue;
+        zero_layout_info info;
+        CHECK(zero_layout_get_info(l, &info) == ZERO_OK);
+        CHECK(info.psi == psi && info.padded_elems == int64_t(N) * info.shard_elems);
+        CHECK(info.shard_elems % A == 0 && info.padding >= 0);
+        std::vector<int64_t> offs(size_t(nt) + 1);
+        if (nt > 0) CHECK(zero_layout_tensor_offsets(l, offs.data(), nt - 1) == ZERO_ERR_CAPACITY);
+        CHECK(zero_layout_tensor_offsets(l, offs.data(), nt) == ZERO_OK);
+        int64_t n = -1;
+        const int rc = zero_layout_segments(l, nullptr, 0, &n);
+        CHECK(rc == (n > 0 ? ZERO_ERR_CAPACITY : ZERO_OK) && n == info.n_segments);
+        std::vector<zero_segment> segs(size_t(n) + 1);
+        CHECK(zero_layout_segments(l, segs.data(), n, &n) == ZERO_OK);
+        int64_t total = 0, prev_end = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            const zero_segment& s = segs[size_t(i)];
+            CHECK(s.len > 0 && s.flat_off == prev_end);
+            CHECK(s.flat_off == offs[size_t(s.tensor)] + s.tensor_off);
+            CHECK(s.shard_off == s.flat_off - int64_t(s.owner) * info.shard_elems);
+            prev_end = s.flat_off + s.len;
+            total += s.len;
+        }
+        CHECK(total == psi);
+        int64_t by_rank = 0;
+        for (int32_t r = 0; r < N; ++r) {
+            int64_t b = 0, re = 0, e = 0, nr = -1;
+            CHECK(zero_layout_rank_range(l, r, &b, &re, &e) == ZERO_OK);
+            CHECK(b == r * info.shard_elems && e == b + info.shard_elems && b <= re && re <= e);
+            const int rr = zero_layout_rank_segments(l, r, nullptr, 0, &nr);
+            CHECK(rr == ZERO_OK || rr == ZERO_ERR_CAPACITY);
+            std::vector<zero_segment> rs(size_t(nr) + 1);
+            CHECK(zero_layout_rank_segments(l, r, rs.data(), nr, &nr) == ZERO_OK);
+            by_rank += nr;
+        }
+        CHECK(by_rank == n);
+        for (int64_t k = 0; k < info.n_fills; ++k) {
+            int64_t nf = -1;
+            const int fr = zero_layout_fill_segments(l, k, nullptr, 0, &nf);
+            CHECK(fr == ZERO_OK || fr == ZERO_ERR_CAPACITY);
+            std::vector<zero_segment> fs(size_t(nf) + 1);
+            CHECK(zero_layout_fill_segments(l, k, fs.data(), nf, &nf) == ZERO_OK);
+        }
+        for (int pp = 0; pp < 2; ++pp) {
+            zero_arena_plan plan;
+            CHECK(zero_arena_plan_for(l, pp, int32_t(next_u64() % 17), B > 0, 4096, &plan) == ZERO_OK);
+            CHECK(plan.total_bytes >= 0);
+        }
+        CHECK(zero_layout_rank_range(l, N, &n, &n, &n) == ZERO_ERR_INVALID_ARG);
+        CHECK(zero_layout_destroy(l) == ZERO_OK);
+    }
+}
+
+static void argument_errors() {
+    zero_layout* l = nullptr;
+    const int64_t bad[2] = {5, -1};
+    CHECK(zero_partition_layout(bad, 2, 2, 0, 1, 0, &l) == ZERO_ERR_INVALID_ARG && !l);
+    const int64_t big[2] = {INT64_MAX - 1, 5};
+    CHECK(zero_partition_layout(big, 2, 2, 0, 1, 0, &l) == ZERO_ERR_INDEX_OVERFLOW && !l);
+    const int64_t one[1] = {100};
+    CHECK(zero_partition_layout(one, 1, 0, 0, 1, 0, &l) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_partition_layout(one, 1, 2, 4, 1, 0, &l) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_partition_layout(one, 1, 2, 0, 0, 0, &l) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_partition_layout(one, 1, 2, 0, 1, -1, &l) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_partition_layout(nullptr, 1, 2, 0, 1, 0, &l) == ZERO_ERR_INVALID_ARG);
+    CHECK(std::strlen(zero_last_error()) > 0);
+    CHECK(zero_layout_destroy(nullptr) == ZERO_OK);
+
+    // the shard step rejects bad arguments before any HIP call
+    const uintptr_t base = uintptr_t(1) << 32;
+    zero_shard_state st;
+    std::memset(&st, 0, sizeof(st));
+    st.shard_elems = 64;
+    st.p[0] = reinterpret_cast<float*>(base);
+    st.m[0] = reinterpret_cast<float*>(base + 4096);
+    st.v[0] = reinterpret_cast<float*>(base + 8192);
+    const uint16_t* grads[2] = {reinterpret_cast<const uint16_t*>(base + 16384),
+                                reinterpret_cast<const uint16_t*>(base + 20480)};
+    uint16_t* slot = reinterpret_cast<uint16_t*>(base + 24576);
+    zero_adam_hparams hp = {1e-4f, 0.9f, 0.999f, 1e-8f, 0.0f};
+    zero_loss_scaler sc = {1024.0f, 0.5f, 2.0f, 1.0f, 1000, 0};
+    int32_t flag = -1;
+    CHECK(zero_shard_step(&st, grads, 0, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_shard_step(&st, grads, 17, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_shard_step(nullptr, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    zero_adam_hparams bad_hp = hp;
+    bad_hp.eps = 0.0f;
+    CHECK(zero_shard_step(&st, grads, 2, &bad_hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    bad_hp = hp;
+    bad_hp.beta1 = NAN;
+    CHECK(zero_shard_step(&st, grads, 2, &bad_hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    zero_loss_scaler bad_sc = sc;
+    bad_sc.scale = INFINITY;
+    CHECK(zero_shard_step(&st, grads, 2, &hp, &bad_sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_shard_step(&st, grads, 2, &hp, &sc, reinterpret_cast<uint16_t*>(base + 100), nullptr,
+                          &flag) == ZERO_ERR_INVALID_ARG);   // slot overlaps p
+    CHECK(zero_shard_step(&st, grads, 2, &hp, &sc, reinterpret_cast<uint16_t*>(base + 24577), nullptr,
+                          &flag) == ZERO_ERR_ALIGNMENT);
+    zero_shard_state st2 = st;
+    st2.p[0] = reinterpret_cast<float*>(base + 8);
+    CHECK(zero_shard_step(&st2, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_ALIGNMENT);
+    CHECK(sc.scale == 1024.0f && st.t == 0 && flag == -1);
+
+    // owner step and reduce-to-owner: unbound and out-of-range arguments
+    const int64_t numel[2] = {10, 20};
+    CHECK(zero_partition_layout(numel, 2, 2, 2, 1, 16, &l) == ZERO_OK);
+    st.shard_elems = 15;
+    CHECK(zero_owner_step(l, 0, &st, &hp, &sc, slot, nullptr, &flag) != ZERO_OK);
+    CHECK(zero_owner_step(nullptr, 0, &st, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    const uint16_t* lists[4] = {grads[0], grads[1], grads[0] + 64, grads[1] + 64};
+    CHECK(zero_layout_bind_contributions(l, 0, lists, nullptr) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_layout_bind_contributions(l, 17, lists, nullptr) == ZERO_ERR_INVALID_ARG);
+    int64_t written = -1;
+    CHECK(zero_reduce_to_owner(l, 0, 0, slot, nullptr, &written) != ZERO_OK);
+    CHECK(zero_pack_bucket(l, 0, slot, nullptr, &written) != ZERO_OK);
+    CHECK(zero_layout_destroy(l) == ZERO_OK);
+
+    // kernel timing before anything was timed
+    float ms = 0.0f;
+    int64_t cnt = -1;
+    CHECK(zero_set_kernel_timing(1) == ZERO_OK);
+    CHECK(zero_last_kernel_ms(&ms) == ZERO_ERR_STATE);
+    CHECK(zero_kernel_times(nullptr, 0, &cnt) == ZERO_OK && cnt == 0);
+    CHECK(zero_set_kernel_timing(0) == ZERO_OK);
+    for (int i = -1; i < 8; ++i) (void)zero_abi_struct_size(i);
+    CHECK(zero_version() == ZERO_PARTITION_VERSION);
+}
+
+static void oracle_calls() {
+    std::vector<uint16_t> h(1 << 16);
+    std::vector<float> f(1 << 16);
+    for (int i = 0; i < (1 << 16); ++i) h[size_t(i)] = uint16_t(i);
+    zo_half_to_float_n(h.data(), f.data(), int64_t(h.size()));
+    std::vector<uint16_t> back(h.size());
+    zo_float_to_half_n(f.data(), back.data(), int64_t(f.size()));
+    for (int i = 0; i < (1 << 16); ++i)
+        if ((i & 0x7C00) != 0x7C00) CHECK(back[size_t(i)] == uint16_t(i));
+    const int64_t n = 4099;
+    for (int R = 1; R <= 16; R += 5) {
+        const size_t nr = static_cast<size_t>(R), ne = static_cast<size_t>(n);
+        std::vector<std::vector<uint16_t>> c(nr, std::vector<uint16_t>(ne));
+        std::vector<const uint16_t*> ptr(nr);
+        for (int r = 0; r < R; ++r) {
+            for (int64_t i = 0; i < n; ++i) c[size_t(r)][size_t(i)] = uint16_t(next_u64() & 0x3BFF);
+            ptr[size_t(r)] = c[size_t(r)].data();
+        }
+        std::vector<float> sum(ne), p(ne, 0.01f), m(ne), v(ne);
+        std::vector<uint16_t> out(ne);
+        zo_reduce(ptr.data(), R, sum.data(), n);
+        CHECK(zo_overflow_flag(ptr.data(), R, n) == 0);
+        zo_adam_apply(ptr.data(), R, p.data(), m.data(), v.data(), out.data(), n, 1024.0f, 1, 1e-4f,
+                      0.9f, 0.999f, 1e-8f, 0.01f);
+        zo_adam_apply(ptr.data(), R, p.data(), m.data(), v.data(), nullptr, n, 1024.0f, 2, 1e-4f,
+                      0.9f, 0.999f, 1e-8f, 0.0f);
+        for (int64_t i = 0; i < n; ++i) CHECK(std::isfinite(p[size_t(i)]));
+        c[0][size_t(n - 1)] = 0x7C00;
+        CHECK(zo_overflow_flag(ptr.data(), R, n) == 1);
+    }
+}
+
+int main() {
+    layouts();
+    argument_errors();
+    oracle_calls();
+    if (g_fail) return 1;
+    std::printf("OK\n");
+    return 0;
+}
