@@ -66,10 +66,6 @@ int blocks_per_cu_step() {
     return v;
 }
 
-int blocks_per_cu_tiled() {
-    static const int v = env_int("ZERO_TILED_BLOCKS_PER_CU", 1, 1, 4096);
-    return v;
-}
 
 
 namespace {
@@ -403,12 +399,12 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         hipError_t e = zp::timing_begin(s);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
         if (pingpong) {
-            e = zp::launch_fused_step(a, ws->cu_count, s);
+            e = zp::launch_fused_step(a, s);
             if (e != hipSuccess) return zp::fail_hip(e, "shard step kernel launch");
         } else {
             e = zp::launch_check(a, ws->cu_count, s);
             if (e != hipSuccess) return zp::fail_hip(e, "check kernel launch");
-            e = zp::launch_update_in_place(a, ws->cu_count, s);
+            e = zp::launch_update_in_place(a, s);
             if (e != hipSuccess) return zp::fail_hip(e, "update kernel launch");
         }
         e = zp::timing_end(s);

@@ -113,23 +113,20 @@ __device__ __forceinline__ void finish_pass(const StepLaunch& a, bool bad) {
 // ---------------------------------------------------------------------------
 // The step kernel (every R from 1 to 16).
 //
-// Each wave owns tiles of 256 H elements, tile t covering [256 H t,
-// 256 H (t+1)).  Lane l holds elements 4l..4l+3 of each of the tile's H
-// 256-element groups, so every load and store instruction of the wave
-// touches one contiguous 1 KiB (fp32) or 512 B (fp16) range.  The grid is
-// persistent (one 256-thread block per CU) and each wave walks its tiles with
-// a register double buffer: the loads of the next tile are in flight while
-// the current tile is computed and stored, so the ALU work overlaps the
-// memory traffic instead of adding to it.  H shrinks as R grows so that the
-// two buffers fit the register file: 4 up to R = 4 (1024-element tiles, which
-// measured 2.5% faster than 512 at R = 2; more waves per SIMD were slower),
-// 2 up to R = 8, 1 beyond.
+// Each wave owns one tile of 1024 elements (four 256-element groups), tile t
+// covering [1024 t, 1024 (t+1)), and the grid holds one wave per tile.  Lane
+// l holds elements 4l..4l+3 of each group, so every load and store
+// instruction of the wave touches one contiguous 1 KiB (fp32) or 512 B (fp16)
+// range.  A wave issues all of its tile's loads, computes, stores and ends;
+// the hardware keeps several such waves per SIMD in flight (77 VGPRs at
+// R = 2, 148 at R = 16) and hands each free slot the next tile.  On the same
+// buffers this ran 3-6% faster for every R than a persistent grid (one block
+// per CU) whose waves walked their tiles with a register double buffer, with
+// the same results bit for bit; 512- and 2048-element tiles ran slower.
 // ---------------------------------------------------------------------------
 
-template <int R>
-constexpr int halves_for() {
-    return R <= 4 ? 4 : (R <= 8 ? 2 : 1);
-}
+constexpr int kTileGroups = 4;                  // 256-element groups per tile
+constexpr int64_t kTile = 256 * kTileGroups;    // elements per tile (one wave)
 
 template <int R, int H>
 struct TileRegs {
@@ -203,29 +200,19 @@ __device__ __forceinline__ void compute_tile(const StepLaunch& a, int64_t base, 
 // kFlag: compute the overflow flag and hand it over (the fused pass).
 // kSkip: in place, after the check pass -- do nothing if the flag holds this
 // call's epoch.
-template <int R, int H, int OUT, bool kFlag, bool kSkip>
-__global__ __launch_bounds__(kThreads) void step_kernel_tiled(const StepLaunch a) {
+template <int R, int OUT, bool kFlag, bool kSkip>
+__global__ __launch_bounds__(kThreads) void step_tile_kernel(const StepLaunch a) {
     if (kSkip && __atomic_load_n(a.flag, __ATOMIC_RELAXED) == a.epoch) return;
-    constexpr int64_t kTile = 256 * H;
     const int lane = threadIdx.x & 63;
     const int64_t ntiles = a.n / kTile;
-    const int64_t waves = int64_t(gridDim.x) * (kThreads / 64);
-    int64_t t = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t t = int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
     bool bad = false;
-    TileRegs<R, H> A, B;
-    if (t < ntiles) load_tile<R, H>(a, t * kTile, lane, A);
-    while (t < ntiles) {
-        int64_t tn = t + waves;
-        if (tn < ntiles) load_tile<R, H>(a, tn * kTile, lane, B);
-        compute_tile<R, H, OUT, kFlag>(a, t * kTile, lane, A, bad);
-        t = tn;
-        if (t >= ntiles) break;
-        tn = t + waves;
-        if (tn < ntiles) load_tile<R, H>(a, tn * kTile, lane, A);
-        compute_tile<R, H, OUT, kFlag>(a, t * kTile, lane, B, bad);
-        t = tn;
+    if (t < ntiles) {
+        TileRegs<R, kTileGroups> regs;
+        load_tile<R, kTileGroups>(a, t * kTile, lane, regs);
+        compute_tile<R, kTileGroups, OUT, kFlag>(a, t * kTile, lane, regs, bad);
     }
-    // the last S mod kTile elements: block 0, one element per thread per pass
+    // the last S mod 1024 elements: block 0, one element per thread per pass
     if (blockIdx.x == 0) {
         for (int64_t e = ntiles * kTile + threadIdx.x; e < a.n; e += kThreads) {
             const float s = reduce1<R>(a, e);
@@ -313,54 +300,51 @@ dim3 grid_for(int64_t n, int cu_count, int per_cu) {
 }
 
 template <bool kFlag, bool kSkip, int R>
-void launch_tiled_r(const StepLaunch& a, int cu_count, hipStream_t s) {
-    constexpr int H = halves_for<R>();
-    const int64_t ntiles = a.n / (256 * H);
+void launch_tiles_r(const StepLaunch& a, hipStream_t s) {
     constexpr int64_t kWavesPerBlock = kThreads / 64;
+    const int64_t ntiles = a.n / kTile;
     int64_t blocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = int64_t(cu_count > 0 ? cu_count : 256) * blocks_per_cu_tiled();
-    if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;   // block 0 also owns the tail
     const dim3 grid{unsigned(blocks)};
     switch (out_class(a.out16)) {
-        case kOut16B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut8B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut4B: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_kernel_tiled<R, H, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut16B: hipLaunchKernelGGL((step_tile_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut8B: hipLaunchKernelGGL((step_tile_kernel<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut4B: hipLaunchKernelGGL((step_tile_kernel<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((step_tile_kernel<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
     }
 }
 
 template <bool kFlag, bool kSkip>
-void launch_step(const StepLaunch& a, int cu_count, hipStream_t s) {
+void launch_step(const StepLaunch& a, hipStream_t s) {
     switch (a.R) {
-        case 1: launch_tiled_r<kFlag, kSkip, 1>(a, cu_count, s); break;
-        case 2: launch_tiled_r<kFlag, kSkip, 2>(a, cu_count, s); break;
-        case 3: launch_tiled_r<kFlag, kSkip, 3>(a, cu_count, s); break;
-        case 4: launch_tiled_r<kFlag, kSkip, 4>(a, cu_count, s); break;
-        case 5: launch_tiled_r<kFlag, kSkip, 5>(a, cu_count, s); break;
-        case 6: launch_tiled_r<kFlag, kSkip, 6>(a, cu_count, s); break;
-        case 7: launch_tiled_r<kFlag, kSkip, 7>(a, cu_count, s); break;
-        case 8: launch_tiled_r<kFlag, kSkip, 8>(a, cu_count, s); break;
-        case 9: launch_tiled_r<kFlag, kSkip, 9>(a, cu_count, s); break;
-        case 10: launch_tiled_r<kFlag, kSkip, 10>(a, cu_count, s); break;
-        case 11: launch_tiled_r<kFlag, kSkip, 11>(a, cu_count, s); break;
-        case 12: launch_tiled_r<kFlag, kSkip, 12>(a, cu_count, s); break;
-        case 13: launch_tiled_r<kFlag, kSkip, 13>(a, cu_count, s); break;
-        case 14: launch_tiled_r<kFlag, kSkip, 14>(a, cu_count, s); break;
-        case 15: launch_tiled_r<kFlag, kSkip, 15>(a, cu_count, s); break;
-        default: launch_tiled_r<kFlag, kSkip, 16>(a, cu_count, s); break;
+        case 1: launch_tiles_r<kFlag, kSkip, 1>(a, s); break;
+        case 2: launch_tiles_r<kFlag, kSkip, 2>(a, s); break;
+        case 3: launch_tiles_r<kFlag, kSkip, 3>(a, s); break;
+        case 4: launch_tiles_r<kFlag, kSkip, 4>(a, s); break;
+        case 5: launch_tiles_r<kFlag, kSkip, 5>(a, s); break;
+        case 6: launch_tiles_r<kFlag, kSkip, 6>(a, s); break;
+        case 7: launch_tiles_r<kFlag, kSkip, 7>(a, s); break;
+        case 8: launch_tiles_r<kFlag, kSkip, 8>(a, s); break;
+        case 9: launch_tiles_r<kFlag, kSkip, 9>(a, s); break;
+        case 10: launch_tiles_r<kFlag, kSkip, 10>(a, s); break;
+        case 11: launch_tiles_r<kFlag, kSkip, 11>(a, s); break;
+        case 12: launch_tiles_r<kFlag, kSkip, 12>(a, s); break;
+        case 13: launch_tiles_r<kFlag, kSkip, 13>(a, s); break;
+        case 14: launch_tiles_r<kFlag, kSkip, 14>(a, s); break;
+        case 15: launch_tiles_r<kFlag, kSkip, 15>(a, s); break;
+        default: launch_tiles_r<kFlag, kSkip, 16>(a, s); break;
     }
 }
 
 }  // namespace
 
-hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream) {
-    launch_step<true, false>(a, cu_count, stream);
+hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream) {
+    launch_step<true, false>(a, stream);
     return hipGetLastError();
 }
 
-hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t stream) {
-    launch_step<false, true>(a, cu_count, stream);
+hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream) {
+    launch_step<false, true>(a, stream);
     return hipGetLastError();
 }
 

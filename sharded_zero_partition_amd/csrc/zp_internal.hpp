@@ -105,7 +105,7 @@ struct StepLaunch {
 // One pass: reduce + finite check + Adam + fp16 cast, reading set *_in and
 // writing set *_out (distinct buffers); raises the flag and publishes it to
 // the host word.
-hipError_t launch_fused_step(const StepLaunch& a, int cu_count, hipStream_t stream);
+hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream);
 
 // In-place mode, pass 1: finite check over the R contributions only; raises
 // the flag and publishes it to the host word.
@@ -113,7 +113,7 @@ hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream);
 
 // In-place mode, pass 2: the update, skipped by every thread when the flag
 // already holds `epoch`.
-hipError_t launch_update_in_place(const StepLaunch& a, int cu_count, hipStream_t stream);
+hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream);
 
 // Rewrite the fp16 slot from the fp32 master values (restores the slot after
 // a skipped ping-pong step): out16[i] = fp16(p_in[i]).
@@ -154,10 +154,8 @@ int check_stream_device(void* stream, int dev, const char* what);
 hipError_t timing_begin(hipStream_t stream);
 hipError_t timing_end(hipStream_t stream);
 
-// Launch shape knobs (blocks per CU of the grid-stride and the pipelined step
-// kernels), read once from ZERO_BLOCKS_PER_CU / ZERO_TILED_BLOCKS_PER_CU when
-// set.
+// Blocks per CU of the grid-stride kernels (the in-place check pass and the
+// slot restore), read once from ZERO_BLOCKS_PER_CU when set.
 int blocks_per_cu_step();
-int blocks_per_cu_tiled();
 
 }  // namespace zp
