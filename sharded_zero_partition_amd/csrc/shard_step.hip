@@ -15,15 +15,14 @@
 //
 // Every element is independent and the kernel moves 26 + 2R bytes per element
 // for about 80 ALU operations, so it is bound by HBM bandwidth.  Design:
-//   - a persistent grid (one 256-thread block per CU) whose waves walk tiles
-//     of 1024, 512 or 256 elements (by R) with a register double buffer --
-//     the loads of the next tile are in flight while the current one is
-//     computed -- and fully coalesced 128/64-bit accesses; a scalar tail for
-//     the elements past the last whole tile;
+//   - one 1024-element tile per wave over a full grid, so the hardware keeps
+//     many short waves in flight and hands each free slot the next tile;
+//     fully coalesced 128/64-bit accesses; a scalar tail for the elements
+//     past the last whole tile;
 //   - the fp32 arithmetic is written in the order of the definition with one
 //     rounding per operation (no contraction, IEEE division and square root),
-//     so the results match a scalar reference bit for bit; with the pipelined
-//     schedule this costs no time (the ALU work hides under the HBM traffic);
+//     so the results match a scalar reference bit for bit; this costs no time
+//     (the ALU work hides under the HBM traffic);
 //   - the overflow flag is a block-level OR followed by one counting atomic
 //     per block; the last block to finish writes the decision into a pinned
 //     host word, and on overflow into the device flag word, which holds the
