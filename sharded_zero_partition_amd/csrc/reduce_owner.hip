@@ -86,9 +86,10 @@ __device__ __forceinline__ u32x4 next_block(const u32x4 v[kU], int u, u32x4 extr
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// What happens to the fp32 sums.  A cooperative span (all 2 x 64 vectors of
-// the wave full and inside the range) ends in `span_pre` (loads the
-// epilogue needs, issued before the contributions' loads) and `span_done`
+// What happens to the fp32 sums.  A span whose 2 x 64 vectors are all full
+// and inside the range starts with `span_pre` (the loads the epilogue needs,
+// issued before the table reads and the contributions' loads); when it also
+// lies in one tensor it ends in `span_done`
 // (the span's sums s[u][e] of shard positions j0 + 512 u + 8 lane + e).
 // Other waves finish vector by vector: `pre` and `vec` for the 8-element
 // vector at shard position jv, `elem` for a single element j.  `finish` is
@@ -277,11 +278,10 @@ constexpr int kGroup = 4;
 
 template <int R, class Epi>
 __device__ __forceinline__ void coop_span(const typename Epi::Launch& a, int src, int64_t rel0,
-                                          int64_t kw, int mis, int lane, bool& bad) {
+                                          int64_t kw, int mis, int lane, bool& bad,
+                                          const typename Epi::SpanPre& pre) {
     constexpr int G = R < kGroup ? R : kGroup;
     const int64_t j0 = kw * 8 - mis;
-    typename Epi::SpanPre pre;
-    Epi::span_pre(a, j0, lane, pre);
     float s[kU][8];
     int64_t dep = 0;   // 0; makes a group's addresses wait for the previous group's sums
 #pragma unroll
@@ -340,6 +340,13 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     const int64_t kw = k_lo + wave * kSpanVec;
     if (kw >= k_end) return;   // the whole wave leaves together
 
+    // A span of full vectors starts its epilogue's own loads (p, m, v for the
+    // owner step) before the table reads below: their addresses need only the
+    // span's position, so their latency overlaps the dependent table reads.
+    const bool full_span = kw * 8 - mis >= j_lo && (kw + kSpanVec) * 8 - mis <= j_hi;
+    typename Epi::SpanPre pre;
+    if (full_span) Epi::span_pre(a, kw * 8 - mis, lane, pre);
+
     // sources of the wave's flat range
     const int64_t k_last = min(kw + kSpanVec, k_end) - 1;
     const int64_t jf = max(kw * 8 - mis, j_lo);
@@ -358,7 +365,6 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     // loads one aligned block per vector group and takes the block after it
     // from the next lane (the last lane from the next group's first lane, or
     // from one extra block after the span).
-    const bool full_span = kw * 8 - mis >= j_lo && (kw + kSpanVec) * 8 - mis <= j_hi;
     if (one && full_span) {
         const int64_t rel0 = a.base + kw * 8 - mis - one_off;    // >= 0, span inside the tensor
         bool in_bounds = true;
@@ -372,7 +378,7 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
         }
         if (in_bounds) {
             // every contribution's loads are issued before the first shuffle
-            coop_span<R, Epi>(a, lo, rel0, kw, mis, lane, bad);
+            coop_span<R, Epi>(a, lo, rel0, kw, mis, lane, bad, pre);
             Epi::finish(a, bad);
             return;
         }
