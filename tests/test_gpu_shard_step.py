@@ -21,7 +21,7 @@ def _p0(rng, S):
 
 @pytest.mark.parametrize("pingpong", [True, False], ids=["pingpong", "inplace"])
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 9, 16])
-@pytest.mark.parametrize("S", [1, 7, 8, 9, 4093, 3 * 65536 + 5])
+@pytest.mark.parametrize("S", [1, 7, 8, 9, 1024, 1025, 4093, 4096, 3 * 65536 + 5])
 def test_small_shards(S, R, pingpong):
     rng = np.random.default_rng(1000 * S + 10 * R + int(pingpong))
     ls = Lockstep(_p0(rng, S), R, HP, 1024.0, pingpong, slot_offset=8, slot_tail=9)
