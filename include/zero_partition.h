@@ -358,10 +358,11 @@ int zero_owner_step(const zero_layout* layout, int32_t rank, zero_shard_state* s
 /* ------------------------------------------------------------------------ */
 
 /* Per calling thread.  While enabled (enable != 0), zero_shard_step,
- * zero_owner_step, zero_pack_bucket and zero_reduce_to_owner record a HIP
- * event before their first and after their last device kernel on the call's
- * stream (for zero_shard_step: the fused pass, or the check and update passes
- * in place; for zero_owner_step: the pass and the flag hand-over).
+ * zero_owner_step, zero_pack_bucket and zero_reduce_to_owner time their
+ * kernels with a pair of HIP events that the launch itself records at the
+ * start of their first kernel and at the end of their last (for
+ * zero_shard_step: the fused pass, or the check and update passes in place;
+ * for zero_owner_step: the pass, without the one-thread flag hand-over).
  * The pairs go into a ring of 4096 per thread, so calls can be timed back to
  * back without waiting on the events; enabling or disabling clears it.
  * zero_last_kernel_ms waits for the most recent pair's end event and returns

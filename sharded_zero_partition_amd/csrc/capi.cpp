@@ -94,9 +94,10 @@ EventPair* current_pair() { return &g_timing.ring[(g_timing.count - 1) % kTiming
 
 }  // namespace
 
-hipError_t timing_begin(hipStream_t stream) {
+hipError_t timing_events(KernelEvents* ev) {
+    ev->start = ev->stop = nullptr;
     if (!g_timing.enabled) return hipSuccess;
-    if (g_timing.open) {   // the previous call failed between its two events: reuse its pair
+    if (g_timing.open) {   // the previous call failed before closing its pair: reuse it
         g_timing.count -= 1;
         g_timing.open = false;
     }
@@ -122,18 +123,14 @@ hipError_t timing_begin(hipStream_t stream) {
         if (e != hipSuccess) return e;
         p.device = dev;
     }
-    e = hipEventRecord(p.start, stream);
-    if (e != hipSuccess) return e;
     g_timing.count += 1;
     g_timing.open = true;
+    ev->start = p.start;
+    ev->stop = p.stop;
     return hipSuccess;
 }
 
-hipError_t timing_end(hipStream_t stream) {
-    if (!g_timing.enabled || !g_timing.open) return hipSuccess;
-    g_timing.open = false;
-    return hipEventRecord(current_pair()->stop, stream);
-}
+void timing_done() { g_timing.open = false; }
 
 namespace {
 
@@ -396,19 +393,19 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         a.R = R;
         zp::step_constants(&a, st, pingpong, hp, sc, out_slot, S, ws);
 
-        hipError_t e = zp::timing_begin(s);
+        zp::KernelEvents ev;
+        hipError_t e = zp::timing_events(&ev);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
         if (pingpong) {
-            e = zp::launch_fused_step(a, s);
+            e = zp::launch_fused_step(a, s, ev);
             if (e != hipSuccess) return zp::fail_hip(e, "shard step kernel launch");
         } else {
-            e = zp::launch_check(a, ws->cu_count, s);
+            e = zp::launch_check(a, ws->cu_count, s, ev.start);
             if (e != hipSuccess) return zp::fail_hip(e, "check kernel launch");
-            e = zp::launch_update_in_place(a, s);
+            e = zp::launch_update_in_place(a, s, ev.stop);
             if (e != hipSuccess) return zp::fail_hip(e, "update kernel launch");
         }
-        e = zp::timing_end(s);
-        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+        zp::timing_done();
         rc = zp::wait_for_flag(ws, s, ws->epoch, &flag);
         if (rc != ZERO_OK) return rc;
         if (!pingpong) {
@@ -476,12 +473,12 @@ extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_sha
         zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, n, ws);
         a.st.R = a.R;
 
-        e = zp::timing_begin(s);
+        zp::KernelEvents ev;
+        e = zp::timing_events(&ev);
         if (e != hipSuccess) return zp::fail_hip(e, "timing event");
-        e = zp::launch_owner_step(a, s);
+        e = zp::launch_owner_step(a, s, ev);
         if (e != hipSuccess) return zp::fail_hip(e, "owner step kernel launch");
-        e = zp::timing_end(s);
-        if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+        zp::timing_done();
         rc = zp::wait_for_flag(ws, s, ws->epoch, &flag);
         if (rc != ZERO_OK) return rc;
         if (flag) {

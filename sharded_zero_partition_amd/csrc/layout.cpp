@@ -436,12 +436,12 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     a.bucket_elems = l->bucket;
     a.bucket = bucket;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    e = zp::timing_begin(st);
+    zp::KernelEvents ev;
+    e = zp::timing_events(&ev);
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");
-    e = zp::launch_pack(a, st);
+    e = zp::launch_pack(a, st, ev);
     if (e != hipSuccess) return zp::fail_hip(e, "pack kernel launch");
-    e = zp::timing_end(st);
-    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+    zp::timing_done();
     if (packed_elems) *packed_elems = std::min(l->bucket, l->psi - a.fill_base);
     return ZERO_OK;
 }
@@ -621,12 +621,12 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     a.base = rank_lo;
     a.shard = shard;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    e = zp::timing_begin(st);
+    zp::KernelEvents ev;
+    e = zp::timing_events(&ev);
     if (e != hipSuccess) return zp::fail_hip(e, "timing event");
-    e = zp::launch_reduce_owner(a, st);
+    e = zp::launch_reduce_owner(a, st, ev);
     if (e != hipSuccess) return zp::fail_hip(e, "reduce kernel launch");
-    e = zp::timing_end(st);
-    if (e != hipSuccess) return zp::fail_hip(e, "timing event");
+    zp::timing_done();
     return ZERO_OK;
 }
 

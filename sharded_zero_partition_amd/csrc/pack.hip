@@ -21,6 +21,8 @@
 // the loads of all U vectors before any is used; vectors that straddle
 // tensors, touch a tensor edge or the end of the stream are gathered element
 // by element.  No LDS staging: each wave's accesses are already contiguous.
+#include <hip/hip_ext.h>
+
 #include "vec16.hpp"
 #include "zp_internal.hpp"
 
@@ -194,14 +196,14 @@ constexpr int kPackSpanU = 2;
 
 }  // namespace
 
-hipError_t launch_pack(const PackLaunch& a, hipStream_t stream) {
+hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     constexpr int64_t kSpan = 512 * kPackSpanU;
     const int64_t waves = (a.bucket_elems + kSpan - 1) / kSpan;
     constexpr int64_t kWavesPerBlock = kPackThreads / 64;
     int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(pack_span_kernel<kPackSpanU>, dim3(unsigned(blocks)), dim3(kPackThreads), 0,
-                       stream, a);
+    hipExtLaunchKernelGGL(pack_span_kernel<kPackSpanU>, dim3(unsigned(blocks)), dim3(kPackThreads), 0,
+                          stream, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@
 // written.  A wave that saw a non-finite sum raises the flag word to the
 // call's epoch; a one-thread kernel afterwards hands the decision to the
 // host.
+#include <hip/hip_ext.h>
+
 #include "adam.hpp"
 #include "vec16.hpp"
 #include "zp_internal.hpp"
@@ -460,49 +462,49 @@ dim3 span_grid(int64_t j_lo, int64_t j_hi, int mis) {
 
 }  // namespace
 
-hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream) {
+hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
     const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, mis);
     switch (a.R) {
-        case 1: hipLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL(reduce_owner_kernel<3>, grid, dim3(kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(reduce_owner_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL(reduce_owner_kernel<5>, grid, dim3(kThreads), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL(reduce_owner_kernel<6>, grid, dim3(kThreads), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL(reduce_owner_kernel<7>, grid, dim3(kThreads), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(reduce_owner_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-        case 9: hipLaunchKernelGGL(reduce_owner_kernel<9>, grid, dim3(kThreads), 0, stream, a); break;
-        case 10: hipLaunchKernelGGL(reduce_owner_kernel<10>, grid, dim3(kThreads), 0, stream, a); break;
-        case 11: hipLaunchKernelGGL(reduce_owner_kernel<11>, grid, dim3(kThreads), 0, stream, a); break;
-        case 12: hipLaunchKernelGGL(reduce_owner_kernel<12>, grid, dim3(kThreads), 0, stream, a); break;
-        case 13: hipLaunchKernelGGL(reduce_owner_kernel<13>, grid, dim3(kThreads), 0, stream, a); break;
-        case 14: hipLaunchKernelGGL(reduce_owner_kernel<14>, grid, dim3(kThreads), 0, stream, a); break;
-        case 15: hipLaunchKernelGGL(reduce_owner_kernel<15>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(reduce_owner_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
+        case 1: hipExtLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 2: hipExtLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 3: hipExtLaunchKernelGGL(reduce_owner_kernel<3>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 4: hipExtLaunchKernelGGL(reduce_owner_kernel<4>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 5: hipExtLaunchKernelGGL(reduce_owner_kernel<5>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 6: hipExtLaunchKernelGGL(reduce_owner_kernel<6>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 7: hipExtLaunchKernelGGL(reduce_owner_kernel<7>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 8: hipExtLaunchKernelGGL(reduce_owner_kernel<8>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 9: hipExtLaunchKernelGGL(reduce_owner_kernel<9>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 10: hipExtLaunchKernelGGL(reduce_owner_kernel<10>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 11: hipExtLaunchKernelGGL(reduce_owner_kernel<11>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 12: hipExtLaunchKernelGGL(reduce_owner_kernel<12>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 13: hipExtLaunchKernelGGL(reduce_owner_kernel<13>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 14: hipExtLaunchKernelGGL(reduce_owner_kernel<14>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 15: hipExtLaunchKernelGGL(reduce_owner_kernel<15>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        default: hipExtLaunchKernelGGL(reduce_owner_kernel<16>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream) {
+hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, 0);
     switch (a.R) {
-        case 1: hipLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(owner_step_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL(owner_step_kernel<3>, grid, dim3(kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(owner_step_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL(owner_step_kernel<5>, grid, dim3(kThreads), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL(owner_step_kernel<6>, grid, dim3(kThreads), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL(owner_step_kernel<7>, grid, dim3(kThreads), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL(owner_step_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
-        case 9: hipLaunchKernelGGL(owner_step_kernel<9>, grid, dim3(kThreads), 0, stream, a); break;
-        case 10: hipLaunchKernelGGL(owner_step_kernel<10>, grid, dim3(kThreads), 0, stream, a); break;
-        case 11: hipLaunchKernelGGL(owner_step_kernel<11>, grid, dim3(kThreads), 0, stream, a); break;
-        case 12: hipLaunchKernelGGL(owner_step_kernel<12>, grid, dim3(kThreads), 0, stream, a); break;
-        case 13: hipLaunchKernelGGL(owner_step_kernel<13>, grid, dim3(kThreads), 0, stream, a); break;
-        case 14: hipLaunchKernelGGL(owner_step_kernel<14>, grid, dim3(kThreads), 0, stream, a); break;
-        case 15: hipLaunchKernelGGL(owner_step_kernel<15>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(owner_step_kernel<16>, grid, dim3(kThreads), 0, stream, a); break;
+        case 1: hipExtLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 2: hipExtLaunchKernelGGL(owner_step_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 3: hipExtLaunchKernelGGL(owner_step_kernel<3>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 4: hipExtLaunchKernelGGL(owner_step_kernel<4>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 5: hipExtLaunchKernelGGL(owner_step_kernel<5>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 6: hipExtLaunchKernelGGL(owner_step_kernel<6>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 7: hipExtLaunchKernelGGL(owner_step_kernel<7>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 8: hipExtLaunchKernelGGL(owner_step_kernel<8>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 9: hipExtLaunchKernelGGL(owner_step_kernel<9>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 10: hipExtLaunchKernelGGL(owner_step_kernel<10>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 11: hipExtLaunchKernelGGL(owner_step_kernel<11>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 12: hipExtLaunchKernelGGL(owner_step_kernel<12>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 13: hipExtLaunchKernelGGL(owner_step_kernel<13>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 14: hipExtLaunchKernelGGL(owner_step_kernel<14>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        case 15: hipExtLaunchKernelGGL(owner_step_kernel<15>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
+        default: hipExtLaunchKernelGGL(owner_step_kernel<16>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

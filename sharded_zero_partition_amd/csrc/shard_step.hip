@@ -29,6 +29,8 @@
 //     epoch of the call that raised it, so it never has to be cleared;
 //   - ping-pong state (read set A, write set B) makes the step a single pass:
 //     the commit is the host flipping the live set once the flag is known.
+#include <hip/hip_ext.h>
+
 #include "adam.hpp"
 #include "vec16.hpp"
 #include "zp_internal.hpp"
@@ -299,61 +301,63 @@ dim3 grid_for(int64_t n, int cu_count, int per_cu) {
 }
 
 template <bool kFlag, bool kSkip, int R>
-void launch_tiles_r(const StepLaunch& a, hipStream_t s) {
+void launch_tiles_r(const StepLaunch& a, hipStream_t s, const KernelEvents& ev) {
     constexpr int64_t kWavesPerBlock = kThreads / 64;
     const int64_t ntiles = a.n / kTile;
     int64_t blocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks < 1) blocks = 1;   // block 0 also owns the tail
     const dim3 grid{unsigned(blocks)};
     switch (out_class(a.out16)) {
-        case kOut16B: hipLaunchKernelGGL((step_tile_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut8B: hipLaunchKernelGGL((step_tile_kernel<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        case kOut4B: hipLaunchKernelGGL((step_tile_kernel<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((step_tile_kernel<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, a); break;
+        case kOut16B: hipExtLaunchKernelGGL((step_tile_kernel<R, kOut16B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, ev.start, ev.stop, 0, a); break;
+        case kOut8B: hipExtLaunchKernelGGL((step_tile_kernel<R, kOut8B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, ev.start, ev.stop, 0, a); break;
+        case kOut4B: hipExtLaunchKernelGGL((step_tile_kernel<R, kOut4B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, ev.start, ev.stop, 0, a); break;
+        default: hipExtLaunchKernelGGL((step_tile_kernel<R, kOut2B, kFlag, kSkip>), grid, dim3(kThreads), 0, s, ev.start, ev.stop, 0, a); break;
     }
 }
 
 template <bool kFlag, bool kSkip>
-void launch_step(const StepLaunch& a, hipStream_t s) {
+void launch_step(const StepLaunch& a, hipStream_t s, const KernelEvents& ev) {
     switch (a.R) {
-        case 1: launch_tiles_r<kFlag, kSkip, 1>(a, s); break;
-        case 2: launch_tiles_r<kFlag, kSkip, 2>(a, s); break;
-        case 3: launch_tiles_r<kFlag, kSkip, 3>(a, s); break;
-        case 4: launch_tiles_r<kFlag, kSkip, 4>(a, s); break;
-        case 5: launch_tiles_r<kFlag, kSkip, 5>(a, s); break;
-        case 6: launch_tiles_r<kFlag, kSkip, 6>(a, s); break;
-        case 7: launch_tiles_r<kFlag, kSkip, 7>(a, s); break;
-        case 8: launch_tiles_r<kFlag, kSkip, 8>(a, s); break;
-        case 9: launch_tiles_r<kFlag, kSkip, 9>(a, s); break;
-        case 10: launch_tiles_r<kFlag, kSkip, 10>(a, s); break;
-        case 11: launch_tiles_r<kFlag, kSkip, 11>(a, s); break;
-        case 12: launch_tiles_r<kFlag, kSkip, 12>(a, s); break;
-        case 13: launch_tiles_r<kFlag, kSkip, 13>(a, s); break;
-        case 14: launch_tiles_r<kFlag, kSkip, 14>(a, s); break;
-        case 15: launch_tiles_r<kFlag, kSkip, 15>(a, s); break;
-        default: launch_tiles_r<kFlag, kSkip, 16>(a, s); break;
+        case 1: launch_tiles_r<kFlag, kSkip, 1>(a, s, ev); break;
+        case 2: launch_tiles_r<kFlag, kSkip, 2>(a, s, ev); break;
+        case 3: launch_tiles_r<kFlag, kSkip, 3>(a, s, ev); break;
+        case 4: launch_tiles_r<kFlag, kSkip, 4>(a, s, ev); break;
+        case 5: launch_tiles_r<kFlag, kSkip, 5>(a, s, ev); break;
+        case 6: launch_tiles_r<kFlag, kSkip, 6>(a, s, ev); break;
+        case 7: launch_tiles_r<kFlag, kSkip, 7>(a, s, ev); break;
+        case 8: launch_tiles_r<kFlag, kSkip, 8>(a, s, ev); break;
+        case 9: launch_tiles_r<kFlag, kSkip, 9>(a, s, ev); break;
+        case 10: launch_tiles_r<kFlag, kSkip, 10>(a, s, ev); break;
+        case 11: launch_tiles_r<kFlag, kSkip, 11>(a, s, ev); break;
+        case 12: launch_tiles_r<kFlag, kSkip, 12>(a, s, ev); break;
+        case 13: launch_tiles_r<kFlag, kSkip, 13>(a, s, ev); break;
+        case 14: launch_tiles_r<kFlag, kSkip, 14>(a, s, ev); break;
+        case 15: launch_tiles_r<kFlag, kSkip, 15>(a, s, ev); break;
+        default: launch_tiles_r<kFlag, kSkip, 16>(a, s, ev); break;
     }
 }
 
 }  // namespace
 
-hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream) {
-    launch_step<true, false>(a, stream);
+hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream, const KernelEvents& ev) {
+    launch_step<true, false>(a, stream, ev);
     return hipGetLastError();
 }
 
-hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream) {
-    launch_step<false, true>(a, stream);
+hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream, hipEvent_t stop) {
+    KernelEvents ev;
+    ev.stop = stop;
+    launch_step<false, true>(a, stream, ev);
     return hipGetLastError();
 }
 
-hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream) {
+hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream, hipEvent_t start) {
     const dim3 grid = grid_for(a.n, cu_count, blocks_per_cu_step());
     switch (a.R) {
-        case 1: hipLaunchKernelGGL(check_kernel<1>, grid, dim3(kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(check_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(check_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL(check_kernel<0>, grid, dim3(kThreads), 0, stream, a); break;
+        case 1: hipExtLaunchKernelGGL(check_kernel<1>, grid, dim3(kThreads), 0, stream, start, nullptr, 0, a); break;
+        case 2: hipExtLaunchKernelGGL(check_kernel<2>, grid, dim3(kThreads), 0, stream, start, nullptr, 0, a); break;
+        case 4: hipExtLaunchKernelGGL(check_kernel<4>, grid, dim3(kThreads), 0, stream, start, nullptr, 0, a); break;
+        default: hipExtLaunchKernelGGL(check_kernel<0>, grid, dim3(kThreads), 0, stream, start, nullptr, 0, a); break;
     }
     return hipGetLastError();
 }

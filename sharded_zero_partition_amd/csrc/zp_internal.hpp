@@ -17,6 +17,12 @@ namespace zp {
 // ---------------------------------------------------------------------------
 int fail(int status, const std::string& msg);
 int fail_hip(hipError_t err, const char* what);
+
+// The events of one timed call (both null when timing is off).
+struct KernelEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
 void clear_error();
 
 // ---------------------------------------------------------------------------
@@ -42,7 +48,7 @@ struct PackLaunch {
     uint16_t* bucket;         // device, 16-byte aligned
 };
 
-hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
+hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEvents& ev);
 
 // ---------------------------------------------------------------------------
 // bucket reduce-to-owner
@@ -64,7 +70,7 @@ struct ReduceLaunch {
     uint16_t* shard;             // device, 2-byte aligned
 };
 
-hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream);
+hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev);
 
 // ---------------------------------------------------------------------------
 // shard step kernels
@@ -105,15 +111,15 @@ struct StepLaunch {
 // One pass: reduce + finite check + Adam + fp16 cast, reading set *_in and
 // writing set *_out (distinct buffers); raises the flag and publishes it to
 // the host word.
-hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream);
+hipError_t launch_fused_step(const StepLaunch& a, hipStream_t stream, const KernelEvents& ev);
 
 // In-place mode, pass 1: finite check over the R contributions only; raises
 // the flag and publishes it to the host word.
-hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream);
+hipError_t launch_check(const StepLaunch& a, int cu_count, hipStream_t stream, hipEvent_t start);
 
 // In-place mode, pass 2: the update, skipped by every thread when the flag
 // already holds `epoch`.
-hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream);
+hipError_t launch_update_in_place(const StepLaunch& a, hipStream_t stream, hipEvent_t stop);
 
 // Rewrite the fp16 slot from the fp32 master values (restores the slot after
 // a skipped ping-pong step): out16[i] = fp16(p_in[i]).
@@ -134,7 +140,7 @@ struct OwnerLaunch : ReduceLaunch {
 // One pass over the range: reduce, Adam (reading set *_in, writing *_out) and
 // the fp16 slot; a wave that saw a non-finite sum raises st.flag to st.epoch.
 // A one-thread kernel after it writes (epoch << 1) | flag to st.host_word.
-hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream);
+hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev);
 
 // The reduce tables bound on `l` (layout.cpp) for an owner step of `rank`:
 // fills every ReduceLaunch member but `shard`, with [g_lo, g_hi) the rank's
@@ -151,8 +157,13 @@ int check_stream_device(void* stream, int dev, const char* what);
 
 // Kernel timing (zero_set_kernel_timing): begin/end mark the first and last
 // kernel of a call on its stream; both are no-ops while timing is disabled.
-hipError_t timing_begin(hipStream_t stream);
-hipError_t timing_end(hipStream_t stream);
+// Kernel timing: while enabled on the calling thread, timing_events hands out
+// the next event pair of the thread's ring (null events otherwise), the
+// launch functions attach its start to their first kernel and its stop to
+// their last (hipExtLaunchKernel records the kernels' own start and end),
+// and timing_done closes the pair once the launches are enqueued.
+hipError_t timing_events(KernelEvents* ev);
+void timing_done();
 
 // Blocks per CU of the grid-stride kernels (the in-place check pass and the
 // slot restore), read once from ZERO_BLOCKS_PER_CU when set.

@@ -27,13 +27,13 @@ static hipError_t never(const char* what) {
     std::fprintf(stderr, "kernel launch reached in a host-only build: %s\n", what);
     std::abort();
 }
-hipError_t launch_pack(const PackLaunch&, hipStream_t) { return never("pack"); }
-hipError_t launch_reduce_owner(const ReduceLaunch&, hipStream_t) { return never("reduce"); }
-hipError_t launch_fused_step(const StepLaunch&, hipStream_t) { return never("step"); }
-hipError_t launch_check(const StepLaunch&, int, hipStream_t) { return never("check"); }
-hipError_t launch_update_in_place(const StepLaunch&, hipStream_t) { return never("update"); }
+hipError_t launch_pack(const PackLaunch&, hipStream_t, const KernelEvents&) { return never("pack"); }
+hipError_t launch_reduce_owner(const ReduceLaunch&, hipStream_t, const KernelEvents&) { return never("reduce"); }
+hipError_t launch_fused_step(const StepLaunch&, hipStream_t, const KernelEvents&) { return never("step"); }
+hipError_t launch_check(const StepLaunch&, int, hipStream_t, hipEvent_t) { return never("check"); }
+hipError_t launch_update_in_place(const StepLaunch&, hipStream_t, hipEvent_t) { return never("update"); }
 hipError_t launch_slot_from_master(const StepLaunch&, int, hipStream_t) { return never("slot"); }
-hipError_t launch_owner_step(const OwnerLaunch&, hipStream_t) { return never("owner"); }
+hipError_t launch_owner_step(const OwnerLaunch&, hipStream_t, const KernelEvents&) { return never("owner"); }
 }  // namespace zp
 
 extern "C" {
