@@ -494,7 +494,7 @@ def main():
                 "kernel_ms_per_fill_event_pairs": round(float(np.mean(fill_ms)), 4),
                 "timing": "kernel_ms_per_fill and roofline: one HIP-event pair around a pass of the "
                           "82 back-to-back launches on the launch stream; event_pairs: one pair per "
-                          "launch (each pair adds a few us)",
+                          "launch, recorded by the launch at its kernel's start and end",
                 "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}}
         play.close()
