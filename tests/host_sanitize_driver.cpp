@@ -2,7 +2,7 @@
 // and the scalar C oracle, built with AddressSanitizer and
 // UndefinedBehaviorSanitizer and driven without a device.
 //
-// The kernel launch functions live in the .hip sources, which this build
+// The kernel launch functions live in the .hip sources, which the sanitized build
 // leaves out: the stubs below stand in for them and fail if reached, since
 // nothing here may launch.  The driver exercises
 //   - partition layouts of seeded random tensor lists: info, offsets, rank
