@@ -7,7 +7,9 @@ ZeRO-2 step uses them, and the degenerate cases of the method.
     chain in the oracle, for every rank of a small model;
   * N = 1 (one rank owns the whole model), shards made only of padding
     (fewer elements than ranks), a bucket larger than the model (one fill
-    with a long zero tail).
+    with a long zero tail);
+  * every call given an explicit side stream rather than torch's current
+    one.
 """
 
 import numpy as np
@@ -117,3 +119,75 @@ def test_bucket_larger_than_model():
     got = bucket.cpu().numpy().view(np.uint16)
     want = oracle.pack_fill([t.cpu().numpy().view(np.uint16) for t in tensors], 0, 1 << 20)
     assert np.array_equal(got, want) and not got[318:].any()
+
+
+def test_every_call_on_an_explicit_side_stream():
+    """Each call of the path given an explicit side stream (not torch's
+    current one): pack, reduce-to-owner, owner step and shard step, each
+    checked bit for bit against the oracle once that stream has drained."""
+    rng = np.random.default_rng(77)
+    numels = [3000, 7, 1, 12345, 640, 0, 2049, 99]
+    n_ranks, bucket, R, scale = 3, 1000, 2, 1024.0
+    hpc = zp.AdamHParams(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay)
+    lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=bucket)
+    olay = OL.partition_layout(numels, n_ranks, 2, 1, bucket)
+    S = olay.shard
+    lists = _rank_lists(rng, numels, R, scale)
+    host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+
+    lay.bind_tensors(lists[0], stream=s)
+    bucket_t = torch.zeros(bucket, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    for k in range(olay.n_fills):
+        lay.pack_bucket(k, bucket_t, stream=s)
+        s.synchronize()
+        want = OL.pack_fill(host[0], k, bucket)
+        assert np.array_equal(bucket_t.cpu().numpy().view(np.uint16), want), k
+
+    lay.bind_contributions(lists, stream=s)
+    for r in range(n_ranks):
+        gshard = torch.zeros(S, dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        want = np.zeros(S, np.uint16)
+        for k in range(olay.n_fills):
+            lay.reduce_to_owner(k, r, gshard, stream=s)
+            off, vals = oracle.reduce_to_owner(host, olay, k, r)
+            want[off:off + vals.size] = vals
+        s.synchronize()
+        assert np.array_equal(gshard.cpu().numpy().view(np.uint16), want), r
+
+        n = max(0, min((r + 1) * S, olay.psi) - r * S)
+        p0 = rng.standard_normal(S, dtype=np.float32) * np.float32(0.02)
+        p = torch.from_numpy(p0).cuda()
+        st = zp.ShardState(p, torch.zeros_like(p), torch.zeros_like(p),
+                           torch.empty_like(p), torch.empty_like(p), torch.empty_like(p))
+        slot = torch.from_numpy(p0.astype(np.float16).view(np.int16)).cuda()
+        sc = zp.LossScaler.make(scale)
+        ost, osc = oracle.ShardState(p0), oracle.LossScaler(scale)
+        out16 = p0.astype(np.float16).view(np.uint16).copy()
+        torch.cuda.synchronize()
+        flag = lay.owner_step(r, st, hpc, sc, slot, stream=s)
+        s.synchronize()
+        assert flag == oracle.owner_step(host, olay, r, ost, osc, HP, out16) == 0
+        for got, wnt in zip(st.live(), (ost.p, ost.m, ost.v)):
+            assert np.array_equal(got[:n].cpu().numpy().view(np.uint32), wnt[:n].view(np.uint32)), r
+        assert np.array_equal(slot.cpu().numpy().view(np.uint16), out16), r
+
+        # the fused shard step on the reduced fp16 shard, same side stream
+        p1 = torch.from_numpy(p0).cuda()
+        st1 = zp.ShardState(p1, torch.zeros_like(p1), torch.zeros_like(p1),
+                            torch.empty_like(p1), torch.empty_like(p1), torch.empty_like(p1))
+        slot1 = torch.empty(S, dtype=torch.int16, device="cuda")
+        sc1 = zp.LossScaler.make(scale)
+        ost1, osc1 = oracle.ShardState(p0), oracle.LossScaler(scale)
+        out1 = np.zeros(S, np.uint16)
+        torch.cuda.synchronize()
+        flag = zp.shard_step(st1, [gshard], hpc, sc1, slot1, stream=s)
+        s.synchronize()
+        assert flag == oracle.shard_step(ost1, [want], osc1, HP, out1) == 0
+        for got, wnt in zip(st1.live(), (ost1.p, ost1.m, ost1.v)):
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), wnt.view(np.uint32)), r
+        assert np.array_equal(slot1.cpu().numpy().view(np.uint16), out1), r
+    lay.close()
