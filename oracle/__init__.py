@@ -14,9 +14,9 @@ Contents
 Every function follows a passage of the ZeRO explainer page (azimuth.plus,
 "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"); the
 citations are in each file.  Parity pins: every function here is pinned by a
-test under tests/ (closed forms, brute force, library routines); the one
-exception is the loss-scale growth rule, which no workload exercises and no
-passage fixes ("parity unpinned").
+test under tests/ (closed forms, brute force, library routines).  The
+loss-scale control, which the pages do not describe, is pinned against
+PyTorch's own dynamic loss-scale update (torch._amp_update_scale_).
 """
 
 import ctypes
@@ -151,8 +151,9 @@ class LossScaler:
     gradients hold any inf/NaN is skipped -- no state changes, the Adam step
     count does not advance -- and the scale is multiplied by `backoff` (not
     below `min_scale`).  After `growth_interval` consecutive taken steps the
-    scale is multiplied by `growth`.  The growth rule is parity unpinned: no
-    passage fixes it and no workload reaches it.
+    scale is multiplied by `growth`, unless that product overflows to inf.
+    This is standard dynamic loss scaling; with min_scale = 0 it matches
+    torch._amp_update_scale_ step for step, which the tests check.
     """
 
     def __init__(self, scale=1024.0, backoff=0.5, growth=2.0, min_scale=1.0,

@@ -217,6 +217,40 @@ def test_loss_scale_trace_of_1t_workload():
     assert ts == [1, 1, 2, 3, 4]
 
 
+def test_loss_scale_matches_torch_amp_update_scale():
+    """The loss-scale control against PyTorch's own dynamic loss-scale update
+    (torch._amp_update_scale_, CPU tensors): on an overflow the scale is
+    multiplied by the backoff factor and the good-step counter reset; after
+    growth_interval consecutive good steps the scale is multiplied by the
+    growth factor (kept when that product is not finite) and the counter
+    reset.  torch has no floor, so the oracle runs with min_scale = 0.
+    Seeded flag sequences with long clean runs and dense overflows, growth
+    intervals 1, 2, 3, 7 and 1000, factors other than 2 and 1/2, and scales
+    near the top and the bottom of the float32 range (growth into inf, backoff
+    into subnormals)."""
+    import torch
+    rng = np.random.default_rng(11)
+    cases = [(65536.0, 2.0, 0.5), (1.0, 3.0, 0.25), (float(np.float32(3.0e38)), 2.0, 0.5),
+             (2.0 ** 127, 4.0, 0.5), (2.0 ** -120, 2.0, 0.5), (1024.0, 1.5, 0.75)]
+    for interval in (1, 2, 3, 7, 1000):
+        for scale0, growth, backoff in cases:
+            for p_over in (0.0, 0.0004, 0.05, 0.5):
+                n = 2600 if interval == 1000 else 300
+                flags = rng.random(n) < p_over
+                sc = oracle.LossScaler(scale0, backoff=backoff, growth=growth, min_scale=0.0,
+                                       growth_interval=interval)
+                ts = torch.tensor([scale0], dtype=torch.float32)
+                tg = torch.zeros(1, dtype=torch.int32)
+                assert float(ts.item()) == sc.scale
+                for i, f in enumerate(flags):
+                    with np.errstate(over="ignore"):
+                        sc.update(bool(f))
+                    torch._amp_update_scale_(ts, tg, torch.tensor([1.0 if f else 0.0]),
+                                             growth, backoff, interval)
+                    assert (sc.scale, sc.good_steps) == (float(ts.item()), int(tg.item())), \
+                        (interval, scale0, growth, backoff, p_over, i)
+
+
 def test_loss_scale_growth_and_floor():
     sc = oracle.LossScaler(8.0, growth_interval=3, min_scale=2.0)
     for _ in range(3):
