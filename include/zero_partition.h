@@ -281,8 +281,15 @@ typedef struct zero_adam_hparams {
 /* Dynamic loss scale.  A step is skipped when any reduced gradient value is
  * inf or NaN: then scale = max(scale * backoff, min_scale), good_steps = 0
  * and no state changes.  A taken step increments good_steps (saturating at INT32_MAX), and when it
- * reaches growth_interval (> 0) the scale is multiplied by growth and
- * good_steps reset. */
+ * reaches growth_interval (> 0) the scale is multiplied by growth (kept when
+ * that product is not finite) and good_steps reset.
+ *
+ * scale and min_scale must be at least ZERO_MIN_LOSS_SCALE (2^-24); calls
+ * with a smaller value fail with ZERO_ERR_INVALID_ARG.  At or above it
+ * 1/scale is finite, and a finite sum of at most 16 fp16 values (below 2^20
+ * in magnitude) unscales to |g| < 2^44, whose square stays far inside the
+ * fp32 range: a clean step never turns a finite gradient into inf or NaN. */
+#define ZERO_MIN_LOSS_SCALE 5.9604644775390625e-08f
 typedef struct zero_loss_scaler {
     float scale;           /* the contributions were multiplied by this */
     float backoff;

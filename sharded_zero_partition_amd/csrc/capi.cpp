@@ -233,11 +233,12 @@ int check_step_scalars(const zero_shard_state* st, const zero_adam_hparams* hp,
     if (has1[1] != *pingpong || has1[2] != *pingpong)
         return fail(ZERO_ERR_INVALID_ARG, "p[1], m[1], v[1] must be all set or all NULL");
     if (!*pingpong && st->cur != 0) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 in place");
-    if (!std::isfinite(sc->scale) || !(sc->scale > 0.0f))
-        return fail(ZERO_ERR_INVALID_ARG, "loss scale must be finite and > 0");
+    if (!std::isfinite(sc->scale) || !(sc->scale >= ZERO_MIN_LOSS_SCALE))
+        return fail(ZERO_ERR_INVALID_ARG, "loss scale must be finite and >= 2^-24");
+    if (!finite_f(sc->min_scale) || !(sc->min_scale >= ZERO_MIN_LOSS_SCALE))
+        return fail(ZERO_ERR_INVALID_ARG, "min_scale must be finite and >= 2^-24");
     if (!finite_f(sc->backoff) || !(sc->backoff > 0.0f) || !finite_f(sc->growth) ||
-        !(sc->growth > 0.0f) || !finite_f(sc->min_scale) || sc->min_scale < 0.0f ||
-        sc->growth_interval < 0 || sc->good_steps < 0)
+        !(sc->growth > 0.0f) || sc->growth_interval < 0 || sc->good_steps < 0)
         return fail(ZERO_ERR_INVALID_ARG, "invalid loss-scaler settings");
     if (!finite_f(hp->lr) || !finite_f(hp->eps) || !(hp->eps > 0.0f) || !finite_f(hp->weight_decay) ||
         !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))

@@ -151,6 +151,11 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(hp=zp.AdamHParams(1e-4, 0.9, 0.999, 0.0, 0.0)) == -1       # eps must be > 0
     assert call(sc=zp.LossScaler.make(0.0)) == -1
     assert call(sc=zp.LossScaler.make(float("inf"))) == -1
+    # the loss-scale floor: scale and min_scale at least 2^-24
+    assert call(sc=zp.LossScaler.make(2.0 ** -25, min_scale=2.0 ** -24)) == -1
+    assert call(sc=zp.LossScaler.make(1024.0, min_scale=0.0)) == -1
+    assert call(sc=zp.LossScaler.make(1024.0, min_scale=2.0 ** -25)) == -1
+    assert b"2^-24" in zp.lib.zero_last_error()
     assert call(slot=ctypes.c_void_p(base + 24577)) == -2             # slot odd address
     assert call(g=(ctypes.c_void_p * 2)(base + 16386, base + 20480)) == -2
     assert call(g=(ctypes.c_void_p * 2)(None, base + 20480)) == -1
@@ -169,6 +174,28 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert b"NULL state" in zp.lib.zero_last_error()
     # nothing was modified
     assert sc.scale == 1024.0 and st.t == 0
+
+
+def test_loss_scale_control_matches_torch_without_device(zp):
+    """The library's own loss-scale control on taken steps, driven through an
+    empty shard (no device work): good_steps counts, growth after
+    growth_interval clean steps, no growth into inf, the step count advances.
+    Checked step by step against torch._amp_update_scale_ (CPU tensors)."""
+    import torch
+    hp = zp.AdamHParams(1e-4, 0.9, 0.999, 1e-8, 0.0)
+    flag = ctypes.c_int32(-1)
+    for scale0, growth, interval in ((1024.0, 2.0, 3), (1.0, 3.0, 1), (2.0 ** 126, 2.0, 2),
+                                     (2.0 ** -24, 1.5, 7), (65536.0, 2.0, 1000)):
+        st = zp.ShardStateC()                       # shard_elems = 0: nothing on the device
+        sc = zp.LossScaler.make(scale0, growth=growth, min_scale=2.0 ** -24, growth_interval=interval)
+        ts = torch.tensor([scale0], dtype=torch.float32)
+        tg = torch.zeros(1, dtype=torch.int32)
+        for i in range(2 * interval + 5 if interval < 1000 else 2100):
+            assert zp.lib.zero_shard_step(ctypes.byref(st), None, 2, ctypes.byref(hp),
+                                          ctypes.byref(sc), None, None, ctypes.byref(flag)) == 0
+            torch._amp_update_scale_(ts, tg, torch.zeros(1), growth, 0.5, interval)
+            assert flag.value == 0 and st.t == i + 1
+            assert (sc.scale, sc.good_steps) == (float(ts.item()), int(tg.item())), (scale0, interval, i)
 
 
 def test_kernel_timing_calls_need_no_device(zp):
