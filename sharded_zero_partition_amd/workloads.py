@@ -92,15 +92,11 @@ class ShardWorkload:
     gather_slots: int = 1              # slots allocated in the gather buffer
     special_step: Optional[int] = None  # 1-based step that gets inf/NaN values
     special_fraction: float = 0.0
-
-    @property
-    def psi(self) -> int:
-        return sum(self.numels)
-
-    @property
-    def shard(self) -> int:
-        per = -(-self.psi // self.n_ranks)
-        return -(-per // self.align) * self.align
+    # Sizes, written out per workload as data (the layout computes them; the
+    # tests check that it reproduces these numbers):
+    psi: int = 0          # elements of the flattened model
+    shard: int = 0        # elements per rank's shard
+    real: int = 0         # elements of this rank's shard inside the model (the rest is padding)
 
 
 @dataclass
@@ -110,41 +106,40 @@ class PackWorkload:
     numels: List[int]
     bucket: int
     n_ranks: int
-
-    @property
-    def psi(self) -> int:
-        return sum(self.numels)
-
-    @property
-    def n_fills(self) -> int:
-        return -(-self.psi // self.bucket)
+    psi: int              # elements of the flattened stream (sum of the drawn sizes)
+    n_fills: int          # bucket fills that cover the stream
 
 
 def tiny() -> ShardWorkload:
     return ShardWorkload("tiny", 1, [1 << 20], n_ranks=4, rank=0, n_contrib=4,
-                         scale=1024.0, steps=3, stage=2, gather_slots=4)
+                         scale=1024.0, steps=3, stage=2, gather_slots=4,
+                         psi=1_048_576, shard=262_144, real=262_144)
 
 
 def gpt2_1p5b() -> ShardWorkload:
     return ShardWorkload("gpt2_1p5b", 2, gpt2_tensor_numels(48, 1600, 6400, 50257),
                          n_ranks=64, rank=63, n_contrib=2, scale=1024.0, steps=10,
-                         stage=2, gather_slots=64)
+                         stage=2, gather_slots=64,
+                         psi=1_557_611_200, shard=24_337_675, real=24_337_675)
 
 
 def zero3_13b() -> ShardWorkload:
     return ShardWorkload("zero3_13b", 3, gpt2_tensor_numels(40, 5120, 20480, 50257),
                          n_ranks=64, rank=63, n_contrib=2, scale=1024.0, steps=5,
-                         stage=3, gather_slots=64)
+                         stage=3, gather_slots=64,
+                         psi=12_848_143_360, shard=200_752_240, real=200_752_240)
 
 
 def pack_20k() -> PackWorkload:
-    return PackWorkload("pack_20k", 4, pack_tensor_numels(), bucket=1 << 26, n_ranks=16)
+    return PackWorkload("pack_20k", 4, pack_tensor_numels(), bucket=1 << 26, n_ranks=16,
+                        psi=5_481_113_944, n_fills=82)
 
 
 def zero3_1t() -> ShardWorkload:
     return ShardWorkload("zero3_1t", 5, [10 ** 12], n_ranks=1024, rank=1023, n_contrib=2,
                          scale=65536.0, steps=5, stage=3, gather_slots=1,
-                         special_step=2, special_fraction=1e-7)
+                         special_step=2, special_fraction=1e-7,
+                         psi=10 ** 12, shard=976_562_500, real=976_562_500)
 
 
 def past_2_31() -> ShardWorkload:
@@ -152,7 +147,8 @@ def past_2_31() -> ShardWorkload:
     2^31 + 4099 elements, so element indices pass the signed 32-bit range and
     the shard ends in a ragged tail; R = 1, scale 1024, 2 steps."""
     return ShardWorkload("past_2_31", 9, [(1 << 31) + 4099], n_ranks=1, rank=0, n_contrib=1,
-                         scale=1024.0, steps=2, stage=3, gather_slots=1)
+                         scale=1024.0, steps=2, stage=3, gather_slots=1,
+                         psi=(1 << 31) + 4099, shard=(1 << 31) + 4099, real=(1 << 31) + 4099)
 
 
 SHARD_WORKLOADS = {w().name: w for w in (tiny, gpt2_1p5b, zero3_13b, zero3_1t)}
@@ -203,10 +199,8 @@ def master_init(w: ShardWorkload, n: int = None, device=None):
     """fp32 master weights of the rank's shard, N(0, 0.02); padding is 0."""
     n = w.shard if n is None else n
     t = normal_f32(n, 0.02, w.wid, KIND_MASTER, 0, w.rank, device)
-    # positions of the shard beyond Psi are padding and hold zeros
-    real = max(0, min(n, w.psi - w.rank * w.shard))
-    if real < n:
-        t[real:] = 0
+    if w.real < n:            # the shard's padding holds zeros
+        t[w.real:] = 0
     return t
 
 
@@ -218,9 +212,8 @@ def grad_contribution(w: ShardWorkload, step: int, index: int, scale: float,
     n = w.shard if n is None else n
     t = normal_f32(n, 1e-3, w.wid, KIND_GRAD, step, index, device)
     t.mul_(np.float32(scale).item())
-    real = max(0, min(n, w.psi - w.rank * w.shard))
-    if real < n:
-        t[real:] = 0
+    if w.real < n:            # no gradient over the shard's padding
+        t[w.real:] = 0
     h = t.to(torch.float16)
     if w.special_step is not None and step == w.special_step:
         pos, vals = special_positions(w, n)

@@ -216,6 +216,20 @@ def test_layout_large_workloads():
     assert (lay.psi, lay.shard, lay.padding, lay.n_fills) == (5_481_113_944, 342_569_622, 8, 82)
 
 
+def test_workload_sizes_are_the_layouts():
+    """The workloads carry their sizes as literal data; the oracle's layout of
+    each workload's tensor list reproduces every one of them."""
+    from sharded_zero_partition_amd import workloads as W
+    for make in (W.tiny, W.gpt2_1p5b, W.zero3_13b, W.zero3_1t, W.past_2_31):
+        w = make()
+        lay = OL.partition_layout(w.numels, w.n_ranks, stage=w.stage, align=w.align)
+        begin, real_end, _ = lay.rank_range(w.rank)
+        assert (w.psi, w.shard, w.real) == (lay.psi, lay.shard, real_end - begin), w.name
+    p = W.pack_20k()
+    lay = OL.partition_layout(p.numels, p.n_ranks, stage=2, bucket=p.bucket)
+    assert (p.psi, p.n_fills) == (lay.psi, lay.n_fills)
+
+
 # ---------------------------------------------------------------------------
 # bucket pack
 # ---------------------------------------------------------------------------
