@@ -72,6 +72,33 @@ def test_float_to_half_random_bits(oracle_lib):
     _same_bits_or_both_nan_f16(got, want)
 
 
+@pytest.mark.slow
+def test_float_to_half_exhaustive(oracle_lib):
+    """Every one of the 2^32 fp32 bit patterns, in chunks over the host's
+    threads (the oracle's C conversion and numpy's cast both release the
+    GIL): equal to numpy's float16 bit for bit, NaN for NaN."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    chunk = 1 << 24
+
+    def check(c):
+        bits = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32)
+        x = bits.view(np.float32)
+        got = oracle_lib.float_to_half(x)
+        with np.errstate(all="ignore"):
+            want = x.astype(np.float16).view(np.uint16)
+        nan_x = np.isnan(x)
+        got_nan = ((got & 0x7C00) == 0x7C00) & ((got & 0x3FF) != 0)
+        want_nan = ((want & 0x7C00) == 0x7C00) & ((want & 0x3FF) != 0)
+        ok = (np.array_equal(got_nan, nan_x) and np.array_equal(want_nan, nan_x)
+              and np.array_equal(got[~nan_x], want[~nan_x]))
+        return c, ok
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as pool:
+        bad = [c for c, ok in pool.map(check, range((1 << 32) // chunk)) if not ok]
+    assert not bad, f"chunks with a difference: {bad[:8]}"
+
+
 def test_float_to_half_special_values(oracle_lib):
     x = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 65519.996, 65520.0,
                   -65520.0, 2.0 ** -24, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -14,
