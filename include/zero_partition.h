@@ -335,13 +335,16 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
  * from the contribution lists bound by zero_layout_bind_contributions, so the
  * Stage 2 reduce of the rank's partition and its Stage 1 update are one pass
  * and no fp16 gradient shard is written in between.  With n = the rank's real
- * elements (min(S, psi - rank*S), or 0) and, for j < n,
- *   sum(j) = c_0(rank*S + j) + ... + c_{R-1}(rank*S + j)
+ * elements (min(S, psi - rank*S), or 0),
+ *   sum(j) = c_0(rank*S + j) + ... + c_{R-1}(rank*S + j)   for j < n
+ *   sum(j) = 0                                             for n <= j < S
  * (fp16 values, fp32 additions from contribution 0 up; c_r as for
- * zero_reduce_to_owner), the flag, the Adam arithmetic, the slot, the skip
- * and the loss-scale rule are those of zero_shard_step over j < n.  Elements
- * [n, S) of the state sets and of the slot are neither read nor written; a
- * rank with n = 0 launches nothing and takes a step (t + 1, cur flipped).
+ * zero_reduce_to_owner; no gradient reaches the padding), the flag, the Adam
+ * arithmetic, the slot, the skip and the loss-scale rule are those of
+ * zero_shard_step over all S elements: the result equals zero_shard_step fed
+ * with the rank's windows of the R flattened lists, zero-filled past the end
+ * of the model.  Padding that starts at 0 therefore stays 0 in the live set
+ * and the slot, whatever the alternate set held.
  *   layout    bucket plan with contributions bound on the current device
  *   rank      0 .. n_ranks - 1: whose partition is updated
  *   st        ping-pong state (p[1], m[1], v[1] set), shard_elems = the

@@ -232,25 +232,13 @@ def owner_step(contrib_lists, lay: Layout, rank: int, state: ShardState, scaler:
 
     contrib_lists holds R lists of fp16 tensors (uint16 bit patterns), one
     list per reducing rank, each with the layout's tensor sizes.  The rank's
-    contributions are the windows [rank*S, rank*S + n) of the R flattened
-    lists, n the real (unpadded) length of its shard; the step is then
-    `shard_step` over those n elements: fp32 sum (rank 0 first), overflow flag
-    over the n sums, Adam and the fp16 slot for elements 0..n-1 of `state` and
-    `out16`.  Padding elements (n..S-1) are left untouched.  This is the Stage
-    2 (P_os+g) reduce-scatter's local arithmetic joined to the Stage 1 update
-    of the rank's own partition, without an fp16 gradient shard in between.
-    Returns the overflow flag."""
+    contributions are the windows [rank*S, (rank+1)*S) of the R flattened
+    lists, zero past the end of the model (the shard's padding receives no
+    gradient); the step is then `shard_step` over all S elements of `state`
+    and `out16`: fp32 sum (rank 0 first), overflow flag, Adam and the fp16
+    slot.  This is the Stage 2 (P_os+g) reduce-scatter's local arithmetic
+    joined to the Stage 1 update of the rank's own partition, without an fp16
+    gradient shard in between.  Returns the overflow flag."""
     lo = rank * lay.shard
-    n = max(0, min(lo + lay.shard, lay.psi) - lo)
-    contribs = [flat_window(lst, lo, lo + n) for lst in contrib_lists]
-    if n == 0:
-        scaler.update(False)
-        state.t += 1
-        return 0
-    flag = overflow_flag(contribs)
-    if not flag:
-        adam_apply(contribs, state.p[:n], state.m[:n], state.v[:n],
-                   None if out16 is None else out16[:n], scaler.scale, state.t + 1, hp)
-        state.t += 1
-    scaler.update(bool(flag))
-    return int(flag)
+    contribs = [flat_window(lst, lo, lo + lay.shard) for lst in contrib_lists]
+    return shard_step(state, contribs, scaler, hp, out16)

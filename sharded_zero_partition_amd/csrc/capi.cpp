@@ -448,12 +448,14 @@ extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_sha
     if (rc != ZERO_OK) return rc;
     if (st->shard_elems != info.shard_elems)
         return fail(ZERO_ERR_INVALID_ARG, "shard_elems differs from the layout's shard size");
-    const int64_t n = a.g_hi - a.g_lo;   // real elements of the rank's shard
+    // the whole shard is written: its real elements from the contributions,
+    // its padding with a zero gradient
+    const int64_t S = st->shard_elems;
 
-    if (n > 0) {
+    if (S > 0) {
         zp::Range rs[7];
         int nr = 0;
-        rc = zp::check_state_arrays(st, pingpong, out_slot, n, rs, &nr);
+        rc = zp::check_state_arrays(st, pingpong, out_slot, S, rs, &nr);
         if (rc != ZERO_OK) return rc;
         for (int i = 0; i < nr; ++i)
             if (zp::contributions_overlap(layout, rs[i].lo, rs[i].hi))
@@ -461,7 +463,7 @@ extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_sha
     }
 
     int32_t flag = 0;
-    if (n > 0) {
+    if (S > 0) {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
@@ -471,7 +473,7 @@ extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_sha
         rc = zp::begin_step(stream, "zero_owner_step", &ws, &lock, &dev);
         if (rc != ZERO_OK) return rc;
         hipStream_t s = static_cast<hipStream_t>(stream);
-        zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, n, ws);
+        zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, S, ws);
         a.st.R = a.R;
 
         zp::KernelEvents ev;

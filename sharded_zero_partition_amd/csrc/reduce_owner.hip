@@ -442,6 +442,22 @@ __global__ __launch_bounds__(kThreads) void owner_step_kernel(const OwnerLaunch 
     owner_body<R, ToAdam>(a);
 }
 
+// The shard's padding, positions [j0, n) of an owner step: no contribution
+// reaches it, so each element takes the Adam step with a zero gradient sum,
+// as the dense shard step does over zero-filled contributions.  Padding is
+// at most N * A - 1 elements except on a rank that holds only padding.
+__global__ __launch_bounds__(kThreads) void owner_pad_kernel(const StepLaunch a, int64_t j0) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t j = j0 + int64_t(blockIdx.x) * kThreads + threadIdx.x; j < a.n; j += stride) {
+        float p = a.p_in[j], m = a.m_in[j], v = a.v_in[j];
+        adam_element(a, 0.0f, p, m, v);
+        a.p_out[j] = p;
+        a.m_out[j] = m;
+        a.v_out[j] = v;
+        a.out16[j] = uint16_t(f2h(p));
+    }
+}
+
 // One thread, launched after the owner step on its stream: copies the pass's
 // decision from the flag word into the pinned host word the host polls.
 __global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsigned long long* host_word) {
@@ -486,7 +502,10 @@ hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const 
     return hipGetLastError();
 }
 
-hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
+namespace {
+
+// The owner step's main pass over the real elements [g_lo, g_hi).
+void launch_owner_real(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, 0);
     switch (a.R) {
         case 1: hipExtLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
@@ -506,8 +525,27 @@ hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const Ker
         case 15: hipExtLaunchKernelGGL(owner_step_kernel<15>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
         default: hipExtLaunchKernelGGL(owner_step_kernel<16>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+}
+
+}  // namespace
+
+hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
+    // the shard is [0, a.st.n): its real elements first, then its padding
+    const int64_t n_real = a.g_hi - a.g_lo;
+    const bool pad = a.st.n > n_real;
+    if (n_real > 0) {
+        launch_owner_real(a, stream, KernelEvents{ev.start, pad ? nullptr : ev.stop});
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (pad) {
+        int64_t blocks = (a.st.n - n_real + kThreads - 1) / kThreads;
+        if (blocks > 2048) blocks = 2048;
+        hipExtLaunchKernelGGL(owner_pad_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                              n_real > 0 ? nullptr : ev.start, ev.stop, 0, a.st, n_real);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(publish_flag_kernel, dim3(1), dim3(1), 0, stream, a.st.flag, a.st.epoch, a.st.host_word);
     return hipGetLastError();
 }

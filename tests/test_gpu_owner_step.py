@@ -3,15 +3,16 @@ the oracle's owner_step: the shard step of one owner fed straight from the R
 ranks' ragged gradient lists.
 
 Bar: overflow flag, step count, loss scale and live-set choice exact; fp32
-master, momentum and variance and the fp16 slot bit-exact over the rank's
-real elements (both sides evaluate the same IEEE operations in the same
-order); padding elements of both state sets and of the slot, and the gather
-buffer around the slot, unchanged.  Cases: small ragged layouts with
+master, momentum and variance and the fp16 slot bit-exact over the whole
+shard, padding included (both sides evaluate the same IEEE operations in the
+same order; the padding takes the step with a zero gradient); the gather
+buffer around the slot unchanged.  Cases: small ragged layouts with
 misaligned tensors, every rank, R = 1..16, several steps with new gradient
 values each; inf/NaN inside and outside the owner's range; a rank that holds
-only padding; the fused shard step on the same sums (cross-check of the two
-kernels); argument errors; and, sampled, the 13B model's rank 63 as the
-benchmark runs it and the 20,000-tensor stream's first and last owner."""
+only padding; zero padding staying zero over NaN-filled alternates and a
+following shard step; the fused shard step on the same sums (cross-check of
+the two kernels); argument errors; and, sampled, the 13B model's rank 63 as
+the benchmark runs it and the 20,000-tensor stream's first and last owner."""
 
 import ctypes
 
@@ -33,7 +34,8 @@ HPC = zp.AdamHParams(HP.lr, HP.beta1, HP.beta2, HP.eps, HP.weight_decay)
 
 class OwnerRun:
     """One owner's device ping-pong state, slot and scaler beside the
-    oracle's.  Set 1 starts as NaN, so a read of it, or of padding, shows."""
+    oracle's.  Set 1 starts as NaN, so a read of it shows; the padding of
+    set 0 holds random values, so leaving it unstepped shows."""
 
     def __init__(self, olay, rank: int, rng, scale=1024.0, slot_offset=3, slot_tail=5, hp=HP):
         self.olay = olay
@@ -51,17 +53,18 @@ class OwnerRun:
         self.gather = torch.full((slot_offset + S + slot_tail,), SENTINEL, dtype=torch.int16, device="cuda")
         self.slot_offset = slot_offset
         self.slot = self.gather[slot_offset:slot_offset + S]
-        # the slot's real part starts as fp16 of the master values
-        self.out16 = np.full(S, SENTINEL, np.uint16)
-        self.out16[:n] = p0[:n].astype(np.float16).view(np.uint16)
+        # the slot starts as fp16 of the master values
+        self.out16 = p0.astype(np.float16).view(np.uint16).copy()
         self.slot.copy_(torch.from_numpy(self.out16.view(np.int16)).cuda())
-        self.pad0 = [x[n:].clone() for x in (self.state.p, self.state.m, self.state.v)]
 
     def step(self, lay, rank, host_lists):
         flag = lay.owner_step(rank, self.state, self.hpc, self.scaler, self.slot)
         torch.cuda.synchronize()
         oflag = oracle.owner_step(host_lists, self.olay, rank, self.ostate, self.oscaler, self.hp, self.out16)
         assert flag == oflag, f"flag {flag} != oracle {oflag}"
+        if oflag:
+            # a skipped step restores the slot to fp16 of the live master
+            self.out16[:] = oracle.float_to_half(self.ostate.p)
         assert self.state.t == self.ostate.t
         assert self.scaler.scale == self.oscaler.scale
         assert self.scaler.good_steps == self.oscaler.good_steps
@@ -69,19 +72,14 @@ class OwnerRun:
         return flag
 
     def compare(self):
-        n = self.n
+        S = self.S
         for name, got, want in zip("pmv", self.state.live(), (self.ostate.p, self.ostate.m, self.ostate.v)):
-            g = got[:n].cpu().numpy()
-            bad = np.flatnonzero(g.view(np.uint32) != want[:n].view(np.uint32))
-            assert bad.size == 0, f"{name}: {bad.size} of {n} differ, first at {bad[0]}: {g[bad[0]]} vs {want[bad[0]]}"
+            g = got.cpu().numpy()
+            bad = np.flatnonzero(g.view(np.uint32) != want.view(np.uint32))
+            assert bad.size == 0, f"{name}: {bad.size} of {S} differ, first at {bad[0]}: {g[bad[0]]} vs {want[bad[0]]}"
         slot = self.slot.cpu().numpy().view(np.uint16)
         bad = np.flatnonzero(slot != self.out16)
         assert bad.size == 0, f"slot: {bad.size} differ, first at {bad[0]}"
-        # padding of both sets untouched
-        for k, x in enumerate((self.state.p, self.state.m, self.state.v)):
-            assert torch.equal(x[n:], self.pad0[k])
-        for x in (self.state.p_alt, self.state.m_alt, self.state.v_alt):
-            assert bool(torch.isnan(x[n:]).all())
         g = self.gather
         assert int((g[:self.slot_offset] != SENTINEL).sum()) == 0
         assert int((g[self.slot_offset + self.S:] != SENTINEL).sum()) == 0
@@ -243,7 +241,9 @@ def test_special_values_inside_and_outside_the_range(value):
     lay.close()
 
 
-def test_padding_only_rank_takes_a_step_without_launching():
+def test_padding_only_rank_steps_its_padding():
+    """A rank that holds only padding takes the step over its padding with a
+    zero gradient (its random master values move by weight decay alone)."""
     rng = np.random.default_rng(8)
     numels = [4, 5]                                     # psi 9, 4 ranks, S = 3: rank 3 all padding
     lay = zp.partition_layout(numels, 4, stage=2, bucket=16)
@@ -252,20 +252,73 @@ def test_padding_only_rank_takes_a_step_without_launching():
     lay.bind_contributions(lists)
     assert olay.shard == 3 and _real(olay, 3) == 0 and _real(olay, 2) == 3
     run = OwnerRun(olay, 3, rng)
-    assert run.step(lay, 3, _host(lists)) == 0
-    assert run.state.t == 1 and run.state.cur == 1
+    for step in range(1, 3):
+        assert run.step(lay, 3, _host(lists)) == 0
+        assert run.state.t == step and run.state.cur == step % 2
+    # 64-byte alignment: ragged padding on the last rank, all-padding ranks after it
+    numels = [1000, 37, 4096, 5, 2500]
+    lay2 = zp.partition_layout(numels, 5, stage=2, align=64, bucket=1024)
+    olay2 = OL.partition_layout(numels, 5, 2, 64, 1024)
+    _, lists2 = _lists(rng, numels, 3)
+    lay2.bind_contributions(lists2)
+    for r in range(5):
+        run = OwnerRun(olay2, r, rng, slot_offset=int(rng.integers(0, 8)))
+        assert run.step(lay2, r, _host(lists2)) == 0
+    lay.close()
+    lay2.close()
+
+
+def test_zero_padding_stays_zero_over_nan_alternates():
+    """Padding that starts at 0 is 0 in the live set and the slot after the
+    flip, although the alternate set it lands in held NaN; a following dense
+    shard step on the same state (zero contributions over the padding) keeps
+    it at 0 in the slot too."""
+    rng = np.random.default_rng(12)
+    numels = [1000, 37, 4096, 5, 2500]                  # psi 7638
+    lay = zp.partition_layout(numels, 3, stage=2, align=64, bucket=1024)
+    S = lay.info.shard_elems                            # 2560: rank 2 has 42 padding elements
+    _, lists = _lists(rng, numels, 2)
+    lay.bind_contributions(lists)
+    r = 2
+    n = sum(numels) - r * S
+    assert 0 < n < S
+    p0 = torch.from_numpy(rng.standard_normal(S, dtype=np.float32) * np.float32(0.02)).cuda()
+    p0[n:] = 0
+    nan = lambda: torch.full_like(p0, float("nan"))     # noqa: E731
+    st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0), nan(), nan(), nan())
+    slot = torch.full((S,), SENTINEL, dtype=torch.int16, device="cuda")
+    slot[:n] = p0[:n].to(torch.float16).view(torch.int16)
+    sc = zp.LossScaler.make(1024.0)
+    assert lay.owner_step(r, st, HPC, sc, slot) == 0 and st.cur == 1
+    torch.cuda.synchronize()
+    for x in st.live():
+        assert int(torch.count_nonzero(x[n:])) == 0 and not bool(torch.isnan(x).any())
+    assert int(torch.count_nonzero(slot[n:])) == 0
+    flat = [torch.cat(lst) for lst in lists]
+    dense = []
+    for f in flat:
+        d = torch.zeros(S, dtype=torch.int16, device="cuda")
+        d[:n] = f[r * S:r * S + n]
+        dense.append(d)
+    assert zp.shard_step(st, dense, HPC, sc, slot) == 0 and st.cur == 0
+    torch.cuda.synchronize()
+    for x in st.live():
+        assert int(torch.count_nonzero(x[n:])) == 0
+    assert int(torch.count_nonzero(slot[n:])) == 0
     lay.close()
 
 
 def test_matches_the_fused_shard_step_on_the_same_sums():
     """The owner step and zero_shard_step are two kernels for one definition:
-    given the rank's windows of the R flattened lists as dense contributions,
-    the shard step must produce the same bits over the real elements."""
+    given the rank's windows of the R flattened lists as dense contributions
+    (zero past the model's end), the shard step must produce the same bits
+    over the whole shard."""
     rng = np.random.default_rng(9)
     numels = [int(x) for x in rng.integers(1, 3000, size=40)]
     R, n_ranks = 3, 4
-    lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=1 << 12)
-    olay = OL.partition_layout(numels, n_ranks, 2, 1, 1 << 12)
+    lay = zp.partition_layout(numels, n_ranks, stage=2, align=64, bucket=1 << 12)
+    olay = OL.partition_layout(numels, n_ranks, 2, 64, 1 << 12)
+    assert olay.padding > 0
     _, lists = _lists(rng, numels, R)
     lay.bind_contributions(lists)
     S = olay.shard
@@ -284,8 +337,8 @@ def test_matches_the_fused_shard_step_on_the_same_sums():
             fb = zp.shard_step(b.state, dense, HPC, b.scaler, b.slot)
             assert fa == fb == 0
         for x, y in zip(a.state.live(), b.state.live()):
-            assert torch.equal(x[:n].view(torch.int32), y[:n].view(torch.int32))
-        assert torch.equal(a.slot[:n], b.slot[:n])
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert torch.equal(a.slot, b.slot)
     lay.close()
 
 
@@ -336,9 +389,9 @@ def test_errors():
 def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1 << 20, plant=None):
     """R whole gradient streams (workloads.gradient_stream), the owner step of
     `rank` for `steps` steps with new streams each step, compared on a sample
-    of the rank's real elements (both range ends, every tensor boundary
-    inside the range, and n_sample random positions) against the oracle's
-    shard step over the sampled sums.  The draws are finite and their
+    of the rank's shard (both ends of its real range, every tensor boundary
+    inside it, n_sample random positions and all of its padding) against the
+    oracle's shard step over the sampled sums (zero over the padding).  The draws are finite and their
     pairwise fp32 sums cannot overflow, so the overflow flag is 0 unless
     `plant` ({step: [(contribution, flat index, fp16 bits)]}) puts a special
     value inside the rank's range on that step; planted positions inside the
@@ -353,10 +406,11 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     inner = offs[(offs > lo) & (offs < lo + n)] - lo
     planted = [g - lo for v in (plant or {}).values() for _, g, _ in v if lo <= g < lo + n]
     pick = np.concatenate([np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n),
-                           inner, inner - 1, rng.integers(0, n, size=n_sample),
-                           np.asarray(planted, np.int64)])
-    sample = np.unique(pick[(pick >= 0) & (pick < n)]).astype(np.int64)
-    g = sample + lo
+                           inner, inner - 1, rng.integers(0, max(n, 1), size=n_sample),
+                           np.asarray(planted, np.int64), np.arange(n, S)])
+    sample = np.unique(pick[(pick >= 0) & (pick < S)]).astype(np.int64)
+    real = sample < n
+    g = sample[real] + lo
     tens = np.searchsorted(offs, g, side="right") - 1
     rel = g - offs[tens]
     p0 = W.normal_f32(S, 0.02, wid, W.KIND_MASTER, 0, rank, "cuda")
@@ -387,7 +441,9 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
         contribs = []
         for buf, starts, _ in streams:
             pos = torch.from_numpy(starts[tens] + rel).cuda()
-            contribs.append(buf[pos].cpu().numpy().view(np.uint16))
+            c = np.zeros(sample.size, np.uint16)            # no gradient over the padding
+            c[real] = buf[pos].cpu().numpy().view(np.uint16)
+            contribs.append(c)
         oracle.shard_step(ost, contribs, osc, HP, out16, flag=want_flag)
         if want_flag:
             # a skipped step restores the slot to fp16 of the live master
@@ -419,8 +475,7 @@ def test_13b_rank63_overflow_sampled():
     the master; the loss scale halves and the next step runs at the new
     scale.  Sampled against the oracle, the planted position included."""
     w = W.zero3_13b()
-    S = -(-sum(w.numels) // w.n_ranks)
-    lo = w.rank * S
+    lo = w.rank * w.shard
     plant = {2: [(1, lo + 12_345_678, 0x7C00), (0, lo - 1000, 0x7E00)]}
     flags = _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3,
                                  n_sample=1 << 18, plant=plant)

@@ -327,37 +327,41 @@ def test_reduce_to_owner_tiles_the_whole_vector():
 
 def test_owner_steps_equal_the_full_vector_step():
     """ZeRO as a drop-in for data parallelism: every rank's owner step, fed
-    from the R ranks' ragged tensor lists, equals (bit for bit, on its real
-    elements) the step of the whole flattened vector; padding is untouched.
-    Special values flag only the owner whose slice holds them (the cross-rank
-    OR belongs to the exchange between GPUs)."""
+    from the R ranks' ragged tensor lists, equals (bit for bit, padding
+    included) the step of the whole flattened vector padded to N*S with zero
+    gradients.  The padding's state is made non-zero here, so that leaving it
+    untouched and updating it with a zero gradient differ.  Special values
+    flag only the owner whose slice holds them (the cross-rank OR belongs to
+    the exchange between GPUs)."""
     rng = np.random.default_rng(23)
     numels = [1000, 3, 0, 777, 4096, 5, 64]
     R, N = 2, 5
     lay = OL.partition_layout(numels, N, stage=2, align=8, bucket=300)
+    assert lay.padding > 0 and lay.rank_range(N - 1)[1] < lay.padded
     lists = [[(rng.standard_normal(n, dtype=np.float32) * np.float32(1.0)).astype(np.float16).view(np.uint16)
               for n in numels] for _ in range(R)]
     hp = oracle.AdamHP(1e-3, 0.9, 0.999, 1e-8, 0.01)
-    p_full = rng.standard_normal(lay.padded, dtype=np.float32) * np.float32(0.05)
-    p_full[lay.psi:] = 0.0
-    full = oracle.ShardState(p_full[:lay.psi])
-    out_full = np.zeros(lay.psi, np.uint16)
-    flat = [np.concatenate(l) for l in lists]
+    NS = lay.padded
+    p_full = rng.standard_normal(NS, dtype=np.float32) * np.float32(0.05)
+    m_full = rng.standard_normal(NS, dtype=np.float32) * np.float32(1e-3)
+    v_full = np.abs(rng.standard_normal(NS, dtype=np.float32)) * np.float32(1e-6)
+    full = oracle.ShardState(p_full, m_full, v_full, t=3)
+    out_full = np.zeros(NS, np.uint16)
+    flat = [np.concatenate([np.concatenate(l), np.zeros(NS - lay.psi, np.uint16)]) for l in lists]
     assert oracle.shard_step(full, flat, oracle.LossScaler(256.0), hp, out_full) == 0
     for r in range(N):
         sl = slice(r * lay.shard, (r + 1) * lay.shard)
-        st = oracle.ShardState(p_full[sl])
+        st = oracle.ShardState(p_full[sl], m_full[sl], v_full[sl], t=3)
         out = np.full(lay.shard, 0x5A5A, np.uint16)
         sc = oracle.LossScaler(256.0)
         assert oracle.owner_step(lists, lay, r, st, sc, hp, out) == 0
-        n = max(0, min(lay.psi - r * lay.shard, lay.shard))
-        g0 = r * lay.shard
-        assert np.array_equal(st.p[:n].view(np.uint32), full.p[g0:g0 + n].view(np.uint32))
-        assert np.array_equal(st.m[:n].view(np.uint32), full.m[g0:g0 + n].view(np.uint32))
-        assert np.array_equal(st.v[:n].view(np.uint32), full.v[g0:g0 + n].view(np.uint32))
-        assert np.array_equal(out[:n], out_full[g0:g0 + n])
-        assert np.array_equal(st.p[n:], p_full[sl][n:]) and (st.m[n:] == 0).all()
-        assert (out[n:] == 0x5A5A).all() and st.t == 1 and sc.good_steps == 1
+        assert np.array_equal(st.p.view(np.uint32), full.p[sl].view(np.uint32))
+        assert np.array_equal(st.m.view(np.uint32), full.m[sl].view(np.uint32))
+        assert np.array_equal(st.v.view(np.uint32), full.v[sl].view(np.uint32))
+        assert np.array_equal(out, out_full[sl])
+        assert st.t == 4 and sc.good_steps == 1
+    # padding moves (zero gradient, non-zero momentum), unlike a skipped element
+    assert not np.array_equal(full.p[lay.psi:], p_full[lay.psi:])
     # an infinity in rank 1's list at flat index g flags owner g // S only
     g = lay.shard + 7
     where = np.searchsorted(np.cumsum(numels), g, side="right")

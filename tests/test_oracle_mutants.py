@@ -191,7 +191,7 @@ INIT_MUTANTS = {
     "backoff_grows_scale": ("np.float32(self.scale * self.backoff)", "np.float32(self.scale * self.growth)", 1),
     "backoff_ignores_floor": ("max(float(np.float32(self.scale * self.backoff)), self.min_scale)",
                               "float(np.float32(self.scale * self.backoff))", 1),
-    "scaler_never_sees_overflow": ("scaler.update(bool(flag))", "scaler.update(False)", 2),
+    "scaler_never_sees_overflow": ("scaler.update(bool(flag))", "scaler.update(False)", 1),
     # loss-scale growth (pinned against torch's dynamic loss-scale update)
     "growth_one_step_late": ("self.good_steps >= self.growth_interval", "self.good_steps > self.growth_interval", 1),
     "growth_one_step_early": ("self.good_steps >= self.growth_interval",
@@ -204,14 +204,17 @@ INIT_MUTANTS = {
                                    "    if True:\n        adam_apply(contribs, state.p, state.m", 1),
     "skipped_step_advances_t": ("        state.t += 1\n    scaler.update(bool(flag))\n    return int(flag)\n\n\ndef reduce_to_owner",
                                 "    state.t += 1\n    scaler.update(bool(flag))\n    return int(flag)\n\n\ndef reduce_to_owner", 1),
-    "step_number_off_by_one": ("state.t + 1, hp)", "state.t + 2, hp)", 2),
+    "step_number_off_by_one": ("state.t + 1, hp)", "state.t + 2, hp)", 1),
     "reduce_to_owner_offset_in_fill": ("return lo - rank * lay.shard, float_to_half(reduce(windows))",
                                        "return lo - fill * lay.bucket, float_to_half(reduce(windows))", 1),
     "reduce_to_owner_reads_rank0_only": ("windows = [flat_window(lst, lo, hi) for lst in contrib_lists]",
                                          "windows = [flat_window(contrib_lists[0], lo, hi) for lst in contrib_lists]", 1),
-    "owner_step_window_off_by_one_rank": ("contribs = [flat_window(lst, lo, lo + n) for lst in contrib_lists]",
-                                          "contribs = [flat_window(lst, lo + lay.shard, lo + lay.shard + n) "
+    "owner_step_window_off_by_one_rank": ("contribs = [flat_window(lst, lo, lo + lay.shard) for lst in contrib_lists]",
+                                          "contribs = [flat_window(lst, lo + lay.shard, lo + 2 * lay.shard) "
                                           "for lst in contrib_lists]", 1),
+    "owner_step_window_off_by_one_element": ("contribs = [flat_window(lst, lo, lo + lay.shard) for lst in contrib_lists]",
+                                             "contribs = [flat_window(lst, lo + 1, lo + 1 + lay.shard) "
+                                             "for lst in contrib_lists]", 1),
 }
 
 
