@@ -10,6 +10,9 @@ Comparison bar (written into the checks below):
   * fp16 slot: bit-exact, and in any case within 1 fp16 ulp.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -78,6 +81,45 @@ class Lockstep:
             t = t[idx]
         return t.cpu().numpy()
 
+    def _oracle_step(self, ch, used, global_flag):
+        """The oracle's shard step on the host copies, over contiguous chunks
+        in parallel threads (its C calls release the GIL): the overflow flag
+        of every chunk first (ORed), then, when no chunk overflowed, Adam on
+        every chunk.  Each element depends only on its own inputs and the
+        shard-wide flag, so this equals one call over the whole shard.  Also
+        returns the state before the step and the unscaled gradients, for the
+        tolerance fallback (None on a skipped step, which must leave the
+        state as it was)."""
+        n = ch[0].size
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cuts = np.linspace(0, n, max(1, min(threads * 4, n // (1 << 18) + 1)) + 1).astype(np.int64)
+        parts = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        st = self.ostate
+        with ThreadPoolExecutor(threads) as pool:
+            if global_flag is None:
+                flag = int(any(pool.map(lambda ab: oracle.overflow_flag([c[ab[0]:ab[1]] for c in ch]), parts)))
+            else:
+                flag = int(global_flag)
+            prev = g = None
+            if not flag:
+                prev = (np.empty_like(st.p), np.empty_like(st.m), np.empty_like(st.v))
+                g = np.empty(n, np.float32)
+                inv = np.float32(1.0 / used)
+
+                def work(ab):
+                    a, b = ab
+                    cc = [c[a:b] for c in ch]
+                    for dst, src in zip(prev, (st.p, st.m, st.v)):
+                        dst[a:b] = src[a:b]
+                    g[a:b] = oracle.reduce(cc) * inv
+                    oracle.adam_apply(cc, st.p[a:b], st.m[a:b], st.v[a:b], self.out16[a:b], used,
+                                      st.t + 1, self.hp)
+
+                list(pool.map(work, parts))
+                st.t += 1
+        self.oscaler.update(bool(flag))
+        return flag, prev, g
+
     def step(self, contribs, global_flag=None):
         """contribs: R device int16 tensors of S fp16 patterns.  global_flag:
         the expected overflow decision when only a sample is compared (the
@@ -87,10 +129,7 @@ class Lockstep:
         flag = zp.shard_step(self.state, contribs, self.hpc, self.scaler, self.slot)
         torch.cuda.synchronize()
         ch = [self._host(c).view(np.uint16) for c in contribs]
-        prev = (self.ostate.p.copy(), self.ostate.m.copy(), self.ostate.v.copy())
-        g = oracle.reduce(ch) * np.float32(1.0 / used)
-        oflag = oracle.shard_step(self.ostate, ch, self.oscaler, self.hp, self.out16,
-                                  flag=global_flag)
+        oflag, prev, g = self._oracle_step(ch, used, global_flag)
         assert flag == oflag, f"overflow flag {flag} != oracle {oflag}"
         assert self.state.t == self.ostate.t
         assert self.scaler.scale == self.oscaler.scale
@@ -101,22 +140,28 @@ class Lockstep:
         self.compare(prev, g)
         return flag
 
+    def _operand_scales(self, prev, g):
+        op = self.ostate.p, self.ostate.m, self.ostate.v
+        if prev is None:
+            return [np.abs(x) for x in op]
+        g_mag = np.abs(g).astype(np.float64) + abs(self.hp.weight_decay) * np.abs(prev[0])
+        sc = adam_operand_scales(prev[1], prev[2], prev[0], g_mag, op[0], self.hp.beta1,
+                                 self.hp.beta2, self.hp.lr, max(self.ostate.t, 1), op[2],
+                                 self.hp.eps)
+        return sc[2], sc[0], sc[1]
+
     def compare(self, prev=None, g=None):
         p, m, v = self.state.live()
-        hp = self._host(p), self._host(m), self._host(v)
         op = self.ostate.p, self.ostate.m, self.ostate.v
-        scales = [np.abs(x) for x in op]
-        if prev is not None:
-            g_mag = np.abs(g).astype(np.float64) + abs(self.hp.weight_decay) * np.abs(prev[0])
-            scales = adam_operand_scales(prev[1], prev[2], prev[0], g_mag, op[0], self.hp.beta1,
-                                         self.hp.beta2, self.hp.lr, max(self.ostate.t, 1), op[2],
-                                         self.hp.eps)
-            scales = (scales[2], scales[0], scales[1])
-        for name, got, want, sc in zip("pmv", hp, op, scales):
-            same = np.array_equal(got.view(np.uint32), want.view(np.uint32))
-            if not same:
+        scales = None                   # only needed when the bits differ
+        for k, (name, dev, want) in enumerate(zip("pmv", (p, m, v), op)):
+            got = self._host(dev)
+            if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
                 self.bit_exact = False
-                assert_scaled_close(got, want, sc, f"{name} (state)")
+                if scales is None:
+                    scales = self._operand_scales(prev, g)
+                assert_scaled_close(got, want, scales[k], f"{name} (state)")
+            del got
         slot = self._host(self.slot).view(np.uint16)
         if not np.array_equal(slot, self.out16):
             self.bit_exact = False

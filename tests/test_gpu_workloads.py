@@ -1,10 +1,10 @@
 """GPU parity on the four shard-step workloads at their full sizes, in the
 launch configuration the benchmark times (single-pass ping-pong state), and
-in place (overflow check pass, then the update pass).  Every element is
-compared where the oracle finishes in seconds (tiny, GPT-2 1.5B); at 13B and
-1T the oracle runs on a sample -- the first and last 8192 elements, one million random ones and every
-injected inf/NaN position -- which is exact because each element's update
-depends only on its own inputs and the global overflow decision."""
+in place (overflow check pass, then the update pass).  Every element of
+every step is compared: the oracle runs over the whole shard in contiguous
+chunks on the host's threads (each element's update depends only on its own
+inputs and the shard-wide overflow decision, which is the OR over the
+chunks), also at 13B (200,752,240 elements) and 1T (976,562,500)."""
 
 import numpy as np
 import pytest
@@ -21,15 +21,6 @@ def _hp(w):
     return oracle.AdamHP(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay)
 
 
-def _sample(S, extra=None, seed=0):
-    rng = np.random.default_rng(seed)
-    idx = np.concatenate([np.arange(min(S, 8192)), np.arange(max(0, S - 8192), S),
-                          rng.integers(0, S, size=min(S, 1_000_000))])
-    if extra is not None:
-        idx = np.concatenate([idx, extra])
-    return np.unique(idx).astype(np.int64)
-
-
 def _gather(w):
     S = w.shard
     g = torch.full((w.gather_slots * S,), 0x5A5A, dtype=torch.int16, device="cuda")
@@ -37,32 +28,18 @@ def _gather(w):
     return g, slot_index * S
 
 
-def _run(w, pingpong, sample=None, full_flag=True):
+def _run(w, pingpong):
     S = w.shard
     print(f"[{w.name}] S={S} R={w.n_contrib} steps={w.steps} pingpong={pingpong}", flush=True)
     gather, off = _gather(w)
     p0 = W.master_init(w, device="cuda")
     ls = Lockstep(p0, w.n_contrib, _hp(w), w.scale, pingpong, slot_offset=off,
-                  slot_tail=gather.numel() - off - S, sample=sample, gather=gather)
+                  slot_tail=gather.numel() - off - S, gather=gather)
     del p0
     for step in range(1, w.steps + 1):
         c = [W.grad_contribution(w, step, r, ls.scaler.scale, device="cuda")
              for r in range(w.n_contrib)]
-        flag = None
-        if sample is not None:
-            if full_flag:
-                flag = oracle.overflow_flag([x.cpu().numpy().view(np.uint16) for x in c])
-            else:
-                # every value outside the injected positions is a finite draw
-                # (checked on the inputs); the sample holds all injected ones
-                pos, _ = W.special_positions(w) if step == w.special_step else (np.zeros(0, np.int64), None)
-                mask = torch.ones(S, dtype=torch.bool, device="cuda")
-                mask[torch.from_numpy(pos).cuda()] = False
-                for x in c:
-                    assert bool(torch.isfinite(x.view(torch.float16)[mask]).all())
-                flag = oracle.overflow_flag([x[torch.from_numpy(sample).cuda()].cpu().numpy()
-                                             .view(np.uint16) for x in c])
-        ls.step(c, global_flag=flag)
+        ls.step(c)
         print(f"[{w.name}] step {step}: flag={ls.flags[-1]} scale={ls.scales[-1]} t={ls.ts[-1]}",
               flush=True)
         del c
@@ -91,7 +68,7 @@ def test_gpt2_1p5b(pingpong):
 def test_zero3_13b(pingpong):
     w = W.zero3_13b()
     assert w.shard == 200_752_240
-    ls = _run(w, pingpong, sample=_sample(w.shard, seed=3))
+    ls = _run(w, pingpong)
     assert ls.flags == [0] * 5 and ls.ts == [1, 2, 3, 4, 5]
     assert ls.bit_exact
 
@@ -102,7 +79,7 @@ def test_zero3_1t_overflow_trace(pingpong):
     assert w.shard == 976_562_500
     pos, vals = W.special_positions(w)
     assert len(pos) == 98
-    ls = _run(w, pingpong, sample=_sample(w.shard, extra=pos, seed=5), full_flag=False)
+    ls = _run(w, pingpong)
     assert ls.flags == [0, 1, 0, 0, 0]
     assert ls.scales == [65536.0, 65536.0, 32768.0, 32768.0, 32768.0]
     assert ls.ts == [1, 1, 2, 3, 4]
