@@ -26,8 +26,13 @@ run also reports
   * the kernel's HBM roofline (algorithmic bytes per launch over the kernel's
     HIP-event time on its stream) and, when the counter profile under
     profiles/ was taken from the current kernel source, its measured traffic,
+  * the achievable line: the step's own access pattern with none of its
+    arithmetic (libzero_probe: same tile-per-wave schedule, 5 read and 4
+    write streams) on the step's own buffers, and a plain copy of the same
+    number of bytes, each timed like the step kernel,
   * torch's device copy of 2 GiB for comparison (a library copy kernel),
-  * the CPU oracle timed on the host on a bounded sample of the same shard.
+  * the CPU oracle timed on the host on the same shard: all of the host's
+    CPU share in threads (the reported baseline) and one thread.
 
 With --shard-workloads it instead times the fused step on every shard
 workload (tiny, GPT-2 1.5B, 13B, 1T) and reports each.
@@ -72,6 +77,39 @@ def measured_traffic(shard_elems: int):
         return None
     return int(round((prof["fetch_kib_per_dispatch"] * prof["fetch_scale"] +
                       prof["write_kib_per_dispatch"] * prof["write_scale"]) * 1024))
+
+
+def host_cpu_share():
+    """(threads, how, cpu_count, model): the CPUs this process may use -- the
+    affinity set, limited by a cgroup CPU quota when there is one, and by the
+    CPU share of one GPU on the GPU machines (16) -- and the CPU model."""
+    count = os.cpu_count() or 1
+    n, how = count, "os.cpu_count()"
+    try:
+        aff = len(os.sched_getaffinity(0))
+        if aff < n:
+            n, how = aff, "sched_getaffinity"
+    except (AttributeError, OSError):
+        pass
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max" and int(quota) // int(period) < n:
+            n, how = max(1, int(quota) // int(period)), "cgroup cpu.max quota"
+    except (OSError, ValueError):
+        pass
+    if n > 16:
+        n, how = 16, "the CPU share of one GPU on the GPU boxes (16 CPUs)"
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, how, count, model
 
 
 def parse_args():
@@ -302,6 +340,41 @@ def main():
     traffic = measured_traffic(S) if args.mode == "pingpong" else None   # profile is of the fused pass
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    # The achievable line on the step's own buffers: the step kernel's access
+    # pattern with none of its arithmetic (reads the contributions and the
+    # live p/m/v, writes the alternate set and the slot: the same 9 streams
+    # and 30 B per element), then a plain copy of the same number of bytes.
+    # Both record HIP events at their kernels' start and end, like the step.
+    achievable = None
+    if args.mode == "pingpong":
+        from sharded_zero_partition_amd import probe
+        lp, lm, lv = st.live()
+        ap, am, av = st.p_alt if st.cur == 0 else st.p, st.m_alt if st.cur == 0 else st.m, \
+            st.v_alt if st.cur == 0 else st.v
+        probe.step_pattern(grads, lp, lm, lv, ap, am, av, slot, reps=2)          # warm-up
+        pat_ms = probe.step_pattern(grads, lp, lm, lv, ap, am, av, slot, reps=args.steps)
+        half = (alg_bytes // 2) // 16 * 16
+        csrc = torch.empty(half, dtype=torch.uint8, device=dev).fill_(7)
+        cdst = torch.empty_like(csrc)
+        probe.copy(csrc, cdst, reps=2)
+        copy_probe_ms = probe.copy(csrc, cdst, reps=args.steps)
+        del csrc, cdst
+        pat_gbs = alg_bytes / (pat_ms * 1e-3) / 1e9
+        cp_gbs = 2 * half / (copy_probe_ms * 1e-3) / 1e9
+        achievable = {
+            "step_pattern": {"ms": round(pat_ms, 4), "achieved": round(pat_gbs, 1), "unit": "GB/s",
+                             "frac_of_peak": round(pat_gbs / HBM_PEAK_GBS, 4),
+                             "what": "zero_probe_step_pattern on the step's own buffers: its "
+                                     "tile-per-wave schedule, 2 fp16 + 3 fp32 read and 3 fp32 + 1 fp16 "
+                                     "written streams (30 B per element), no arithmetic; mean kernel "
+                                     f"time of {args.steps} launches"},
+            "copy": {"ms": round(copy_probe_ms, 4), "achieved": round(cp_gbs, 1), "unit": "GB/s",
+                     "frac_of_peak": round(cp_gbs / HBM_PEAK_GBS, 4),
+                     "what": f"zero_probe_copy of {half} bytes into fresh buffers ({2 * half} bytes "
+                             f"moved, the step's algorithmic bytes); mean kernel time of {args.steps} launches"},
+            "step_over_pattern": round(achieved / pat_gbs, 4),
+            "step_over_copy": round(achieved / cp_gbs, 4)}
 
     # The rank's whole local share of one iteration at 13B: its full fp16
     # gradient stream (the model's 484 tensors, packed bucket by bucket for the
@@ -552,7 +625,7 @@ def main():
 
     # CPU oracle on a bounded sample of the same shard (first step's inputs)
     cpu = None
-    cpu_threads = None
+    cpu_one = None
     if cpu_inputs is not None:
         import oracle
         p_host, c_host = cpu_inputs
@@ -562,16 +635,17 @@ def main():
         oracle.shard_step(ost, c_host, oracle.LossScaler(w.scale),
                           oracle.AdamHP(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay), out16)
         cpu_s = time.perf_counter() - t0
-        cpu = {"value": round(cpu_n / cpu_s, 1), "unit": "elements/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"the whole rank-63 shard ({cpu_n} elements), first step "
-                         f"(scalar C oracle, one thread, {cpu_s:.1f} s)"}
+        cpu_one = {"value": round(cpu_n / cpu_s, 1), "unit": "elements/s", "cores": 1,
+                   "kind": "oracle",
+                   "sample": f"the whole rank-63 shard ({cpu_n} elements), first step "
+                             f"(scalar C oracle, one thread, {cpu_s:.1f} s)"}
 
         # The same C functions over contiguous chunks in parallel threads (the
-        # calls release the GIL): the overflow flag over every chunk first,
-        # then Adam on every chunk when no chunk overflowed.
+        # calls release the GIL), one per CPU of the host's share: the
+        # overflow flag over every chunk first, then Adam on every chunk when
+        # no chunk overflowed.
         from concurrent.futures import ThreadPoolExecutor
-        n_threads = max(1, min(16, os.cpu_count() or 1))
+        n_threads, share_how, cpu_count, cpu_model = host_cpu_share()
         bounds = np.linspace(0, cpu_n, n_threads + 1).astype(np.int64)
         par = oracle.ShardState(p_host)
         par_out = np.empty(cpu_n, np.uint16)
@@ -586,11 +660,13 @@ def main():
                     par.v[ab[0]:ab[1]], par_out[ab[0]:ab[1]], w.scale, 1, ohp), parts))
         par_s = time.perf_counter() - t0
         assert np.array_equal(par_out, out16) and np.array_equal(par.p.view(np.uint32), ost.p.view(np.uint32))
-        cpu_threads = {"value": round(cpu_n / par_s, 1), "unit": "elements/s", "cores": n_threads,
-                       "kind": "oracle",
-                       "sample": f"the same shard and step, the oracle's C functions over {len(parts)} "
-                                 f"contiguous chunks in {n_threads} threads ({par_s:.2f} s); results "
-                                 "equal to the one-thread run"}
+        cpu = {"value": round(cpu_n / par_s, 1), "unit": "elements/s", "cores": n_threads,
+               "kind": "oracle",
+               "sample": f"the whole rank-63 shard ({cpu_n} elements), first step: the oracle's C "
+                         f"functions over {len(parts)} contiguous chunks in {n_threads} threads "
+                         f"({par_s:.2f} s); results equal to the one-thread run",
+               "cpu_model": cpu_model, "cpu_count": cpu_count,
+               "threads_from": share_how}
 
     out = {
         "metric": METRIC,
@@ -615,6 +691,7 @@ def main():
         "kernel_ms_min": round(float(np.min(kernel_ms)), 4),
         "kernel_ms_median": round(float(np.median(kernel_ms)), 4),
         "roofline": roofline,
+        "achievable": achievable,
         "placement_spread": placement,
         "library_copy": library_copy,
         "rank_iteration": rank_iteration,
@@ -623,7 +700,7 @@ def main():
         "reduce_to_owner": reduce_owner,
         "owner_step": owner,
         "cpu_baseline": cpu,
-        "cpu_baseline_threads": cpu_threads,
+        "cpu_baseline_one_thread": cpu_one,
     }
     print(json.dumps(out), flush=True)
 

@@ -1,8 +1,10 @@
-"""Build libzero_partition.so (HIP kernels + C ABI) for gfx950 with hipcc.
+"""Build libzero_partition.so (HIP kernels + C ABI) and libzero_probe.so (the
+achievable-bandwidth probes the benchmark reports beside the step) for gfx950
+with hipcc.
 
 Run `python -m sharded_zero_partition_amd.build` (or call build()).  Objects
-go to _build/ at the repository root; the shared library is written next to
-this file, where the Python binding loads it.
+go to _build/ at the repository root; the shared libraries are written next
+to this file, where the Python bindings load them.
 """
 
 import os
@@ -17,8 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero_partition.so")
+PROBE_LIB = os.path.join(PKG, "libzero_probe.so")
 
 SOURCES = ["layout.cpp", "capi.cpp", "pack.hip", "shard_step.hip", "reduce_owner.hip"]
+PROBE_SOURCES = ["stream_probe.hip"]
 
 ARCH = "gfx950"
 
@@ -52,16 +56,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                    check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

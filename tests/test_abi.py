@@ -26,8 +26,8 @@ def zp():
     return z
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(zero_\w+)\s*\(", text)))
 
@@ -39,6 +39,25 @@ def test_every_declared_symbol_is_exported(zp):
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
     assert set(names) == set(zp.binding.SIGNATURES), "binding and header disagree"
+
+
+def test_every_header_is_a_built_library():
+    """Each header under include/ declares one library's functions, and that
+    library exports every one of them (the probe library loads without a
+    device too)."""
+    from sharded_zero_partition_amd import build as zbuild
+    libs = {"zero_partition.h": zbuild.LIB, "zero_probe.h": zbuild.PROBE_LIB}
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == sorted(libs)
+    if not all(os.path.exists(p) for p in libs.values()):
+        zbuild.build()
+    for h, path in libs.items():
+        names = _declared_functions(os.path.join(ROOT, "include", h))
+        lib = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(lib, n), f"{n} declared in {h} but not exported by {os.path.basename(path)}"
+    from sharded_zero_partition_amd import probe
+    assert set(_declared_functions(os.path.join(ROOT, "include", "zero_probe.h"))) == set(probe.SIGNATURES)
 
 
 def test_struct_sizes_and_version(zp):
