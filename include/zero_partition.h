@@ -290,6 +290,11 @@ typedef struct zero_adam_hparams {
  * in magnitude) unscales to |g| < 2^44, whose square stays far inside the
  * fp32 range: a clean step never turns a finite gradient into inf or NaN. */
 #define ZERO_MIN_LOSS_SCALE 5.9604644775390625e-08f
+
+/* Largest shard a step call takes (4096 * (2^31 - 1) elements, about 8.8e12):
+ * a pass is one launch of at most 2^31 - 1 workgroups of 4096 elements.
+ * Larger shard_elems fail with ZERO_ERR_INVALID_ARG. */
+#define ZERO_MAX_SHARD_ELEMS 8796093018112LL
 typedef struct zero_loss_scaler {
     float scale;           /* the contributions were multiplied by this */
     float backoff;
@@ -330,6 +335,26 @@ typedef struct zero_loss_scaler {
 int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
                     const zero_adam_hparams* hp, zero_loss_scaler* scaler,
                     uint16_t* out_slot, void* stream, int32_t* overflow);
+
+/* zero_shard_step for callers that cannot allocate memory (code that must
+ * not call hipMalloc or hipHostMalloc: tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, arithmetic, results, errors and
+ * state/scaler updates as zero_shard_step, bit for bit, on the same kernels.
+ * What differs: the flag word, the blocks-done counter and the decision word
+ * live in a fixed 256-byte device array of the library (one copy per device
+ * and process, kept until the process ends) instead of a workspace allocated
+ * on a device's first call, and the call clears those words on `stream`,
+ * copies the 8-byte decision back into host memory after the pass and waits
+ * for `stream` (zero_shard_step instead polls a pinned host word).  The array
+ * keeps the last call's contents; calls on one device are serialised by the
+ * library within a process, so they never share the words at the same time.
+ * The call allocates nothing (no hipMalloc, hipHostMalloc or event) and does
+ * not take part in kernel timing.  The words are the same for every shard
+ * size: the largest shard is ZERO_MAX_SHARD_ELEMS, as for zero_shard_step.
+ * Errors: as zero_shard_step. */
+int zero_shard_step_noalloc(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
+                            const zero_adam_hparams* hp, zero_loss_scaler* scaler,
+                            uint16_t* out_slot, void* stream, int32_t* overflow);
 
 /* Owner step: zero_shard_step in ping-pong mode with the sum taken straight
  * from the contribution lists bound by zero_layout_bind_contributions, so the

@@ -13,7 +13,7 @@ Names follow the C ABI in include/zero_partition.h:
   Layout.pack_bucket(...)              (zero_pack_bucket)
   Layout.bind_contributions(...)       (zero_layout_bind_contributions)
   Layout.reduce_to_owner(...)          (zero_reduce_to_owner)
-  shard_step(...), PreparedStep(...)   (zero_shard_step)
+  shard_step(...), PreparedStep(...)   (zero_shard_step; zero_shard_step_noalloc with noalloc=True)
   Layout.owner_step(...)               (zero_owner_step)
   set_kernel_timing, last_kernel_ms, kernel_times   (kernel timing)
 """
@@ -121,6 +121,7 @@ SIGNATURES = {
     "zero_layout_bind_contributions": (ctypes.c_int, [_P, _I32, _P, _P]),
     "zero_reduce_to_owner": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "zero_shard_step": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
+    "zero_shard_step_noalloc": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P]),
     "zero_owner_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P]),
     "zero_set_kernel_timing": (ctypes.c_int, [_I32]),
     "zero_last_kernel_ms": (ctypes.c_int, [_P]),
@@ -393,9 +394,9 @@ class ShardState:
 
 
 def shard_step(state: ShardState, grads, hparams: AdamHParams, scaler: LossScaler, out_slot,
-               stream=None) -> int:
-    """zero_shard_step: returns the overflow flag; updates state.t, state.cur
-    and the scaler in place."""
+               stream=None, noalloc: bool = False) -> int:
+    """zero_shard_step (zero_shard_step_noalloc with noalloc=True): returns
+    the overflow flag; updates state.t, state.cur and the scaler in place."""
     R = len(grads)
     S = state.shard_elems
     dev = _current_device()
@@ -409,8 +410,8 @@ def shard_step(state: ShardState, grads, hparams: AdamHParams, scaler: LossScale
     c = state._to_c(dev)
     flag = ctypes.c_int32()
     slot = ctypes.c_void_p(_dev_ptr(out_slot, "out_slot", 2, dev) if S else None)
-    _check(lib.zero_shard_step(_ref(c), ptrs, R, _ref(hparams), _ref(scaler), slot,
-                               _stream_ptr(stream), _ref(flag)))
+    fn = lib.zero_shard_step_noalloc if noalloc else lib.zero_shard_step
+    _check(fn(_ref(c), ptrs, R, _ref(hparams), _ref(scaler), slot, _stream_ptr(stream), _ref(flag)))
     state.t = c.t
     state.cur = c.cur
     return flag.value

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzero_partition.so")
 PROBE_LIB = os.path.join(PKG, "libzero_probe.so")
 
-SOURCES = ["layout.cpp", "capi.cpp", "pack.hip", "shard_step.hip", "reduce_owner.hip"]
+SOURCES = ["layout.cpp", "capi.cpp", "pack.hip", "shard_step.hip", "reduce_owner.hip", "noalloc.hip"]
 PROBE_SOURCES = ["stream_probe.hip"]
 
 ARCH = "gfx950"

@@ -151,6 +151,7 @@ struct DeviceWorkspace {
 constexpr int kMaxDevices = 64;
 std::mutex g_ws_mu;
 DeviceWorkspace* g_ws[kMaxDevices] = {};
+std::mutex g_noalloc_mu[kMaxDevices];   // zero_shard_step_noalloc, per device
 
 int get_workspace(int dev, DeviceWorkspace** out) {
     if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_ERR_INVALID_ARG, "device index out of range");
@@ -224,7 +225,8 @@ int check_step_scalars(const zero_shard_state* st, const zero_adam_hparams* hp,
                        const zero_loss_scaler* sc, bool* pingpong) {
     const int64_t S = st->shard_elems;
     if (S < 0) return fail(ZERO_ERR_INVALID_ARG, "shard_elems < 0");
-    if (S > std::numeric_limits<int64_t>::max() / 16) return fail(ZERO_ERR_INDEX_OVERFLOW, "shard too large");
+    if (S > ZERO_MAX_SHARD_ELEMS)
+        return fail(ZERO_ERR_INVALID_ARG, "shard_elems above ZERO_MAX_SHARD_ELEMS (one launch's grid)");
     if (st->cur != 0 && st->cur != 1) return fail(ZERO_ERR_INVALID_ARG, "cur must be 0 or 1");
     if (st->t < 0 || st->t == std::numeric_limits<int64_t>::max())
         return fail(ZERO_ERR_INVALID_ARG, "step count out of range");
@@ -296,9 +298,9 @@ int begin_step(void* stream, const char* who, DeviceWorkspace** ws, std::unique_
 }
 
 // State pointers and Adam constants for step t + 1 (used only if the step is
-// taken); the flag words of `ws` at its current epoch.
+// taken).
 void step_constants(StepLaunch* a, const zero_shard_state* st, bool pingpong, const zero_adam_hparams* hp,
-                    const zero_loss_scaler* sc, uint16_t* out_slot, int64_t n, const DeviceWorkspace* ws) {
+                    const zero_loss_scaler* sc, uint16_t* out_slot, int64_t n) {
     const int64_t t_new = st->t + 1;
     const int cur = st->cur;
     a->p_in = st->p[cur];
@@ -319,6 +321,10 @@ void step_constants(StepLaunch* a, const zero_shard_state* st, bool pingpong, co
     a->bias_corr2 = float(1.0 - std::pow(double(hp->beta2), double(t_new)));
     a->eps = hp->eps;
     a->weight_decay = hp->weight_decay;
+}
+
+// The flag words of `ws` at its current epoch.
+void workspace_words(StepLaunch* a, const DeviceWorkspace* ws) {
     a->flag = ws->d_flag;
     a->epoch = ws->epoch;
     a->done = reinterpret_cast<unsigned long long*>(ws->d_flag + 16);
@@ -344,6 +350,34 @@ void commit_step(zero_shard_state* st, bool pingpong, zero_loss_scaler* sc, int3
     }
 }
 
+// Argument checks of a shard step call (nothing is modified).
+int check_shard_step_call(const zero_shard_state* st, const uint16_t* const* grads, int32_t R,
+                          const zero_adam_hparams* hp, const zero_loss_scaler* sc, const uint16_t* out_slot,
+                          const char* who, bool* pingpong) {
+    if (!st || !hp || !sc) return fail(ZERO_ERR_INVALID_ARG, std::string(who) + ": NULL state, hparams or scaler");
+    if (R < 1 || R > kMaxContrib) return fail(ZERO_ERR_INVALID_ARG, "R must be in 1..16");
+    int rc = check_step_scalars(st, hp, sc, pingpong);
+    if (rc != ZERO_OK) return rc;
+    const int64_t S = st->shard_elems;
+    if (S == 0) return ZERO_OK;
+    if (!grads) return fail(ZERO_ERR_INVALID_ARG, "grads is NULL");
+    for (int r = 0; r < R; ++r) {
+        if (!grads[r]) return fail(ZERO_ERR_INVALID_ARG, "a gradient pointer is NULL");
+        if (!aligned(grads[r], 16)) return fail(ZERO_ERR_ALIGNMENT, "gradient not 16-byte aligned");
+    }
+    Range rs[7];
+    int nr = 0;
+    rc = check_state_arrays(st, *pingpong, out_slot, S, rs, &nr);
+    if (rc != ZERO_OK) return rc;
+    for (int r = 0; r < R; ++r) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(grads[r]);
+        const Range g = {lo, lo + uintptr_t(S) * 2};
+        for (int i = 0; i < nr; ++i)
+            if (overlap(g, rs[i])) return fail(ZERO_ERR_INVALID_ARG, "a gradient overlaps a written array");
+    }
+    return ZERO_OK;
+}
+
 }  // namespace
 }  // namespace zp
 
@@ -353,31 +387,10 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
                                const zero_adam_hparams* hp, zero_loss_scaler* sc,
                                uint16_t* out_slot, void* stream, int32_t* overflow) {
     zp::clear_error();
-    if (!st || !hp || !sc) return fail(ZERO_ERR_INVALID_ARG, "zero_shard_step: NULL state, hparams or scaler");
-    if (R < 1 || R > zp::kMaxContrib) return fail(ZERO_ERR_INVALID_ARG, "R must be in 1..16");
     bool pingpong = false;
-    int rc = zp::check_step_scalars(st, hp, sc, &pingpong);
+    int rc = zp::check_shard_step_call(st, grads, R, hp, sc, out_slot, "zero_shard_step", &pingpong);
     if (rc != ZERO_OK) return rc;
     const int64_t S = st->shard_elems;
-
-    if (S > 0) {
-        if (!grads) return fail(ZERO_ERR_INVALID_ARG, "grads is NULL");
-        for (int r = 0; r < R; ++r) {
-            if (!grads[r]) return fail(ZERO_ERR_INVALID_ARG, "a gradient pointer is NULL");
-            if (!zp::aligned(grads[r], 16)) return fail(ZERO_ERR_ALIGNMENT, "gradient not 16-byte aligned");
-        }
-        zp::Range rs[7];
-        int nr = 0;
-        rc = zp::check_state_arrays(st, pingpong, out_slot, S, rs, &nr);
-        if (rc != ZERO_OK) return rc;
-        for (int r = 0; r < R; ++r) {
-            const uintptr_t lo = reinterpret_cast<uintptr_t>(grads[r]);
-            const zp::Range g = {lo, lo + uintptr_t(S) * 2};
-            for (int i = 0; i < nr; ++i)
-                if (zp::overlap(g, rs[i]))
-                    return fail(ZERO_ERR_INVALID_ARG, "a gradient overlaps a written array");
-        }
-    }
 
     int32_t flag = 0;
     if (S > 0) {
@@ -392,7 +405,8 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         std::memset(&a, 0, sizeof(a));
         for (int r = 0; r < R; ++r) a.grad[r] = grads[r];
         a.R = R;
-        zp::step_constants(&a, st, pingpong, hp, sc, out_slot, S, ws);
+        zp::step_constants(&a, st, pingpong, hp, sc, out_slot, S);
+        zp::workspace_words(&a, ws);
 
         zp::KernelEvents ev;
         hipError_t e = zp::timing_events(&ev);
@@ -419,6 +433,75 @@ extern "C" int zero_shard_step(zero_shard_state* st, const uint16_t* const* grad
         if (flag && pingpong) {
             // the pass wrote the slot speculatively; restore fp16(master)
             e = zp::launch_slot_from_master(a, ws->cu_count, s);
+            if (e != hipSuccess) return zp::fail_hip(e, "slot restore kernel launch");
+        }
+    }
+
+    zp::commit_step(st, pingpong, sc, flag);
+    if (overflow) *overflow = flag;
+    return ZERO_OK;
+}
+
+extern "C" int zero_shard_step_noalloc(zero_shard_state* st, const uint16_t* const* grads, int32_t R,
+                                       const zero_adam_hparams* hp, zero_loss_scaler* sc,
+                                       uint16_t* out_slot, void* stream, int32_t* overflow) {
+    zp::clear_error();
+    bool pingpong = false;
+    int rc = zp::check_shard_step_call(st, grads, R, hp, sc, out_slot, "zero_shard_step_noalloc", &pingpong);
+    if (rc != ZERO_OK) return rc;
+    const int64_t S = st->shard_elems;
+
+    int32_t flag = 0;
+    if (S > 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
+        rc = zp::check_stream_device(stream, dev, "zero_shard_step_noalloc");
+        if (rc != ZERO_OK) return rc;
+        if (dev >= zp::kMaxDevices) return fail(ZERO_ERR_INVALID_ARG, "device index out of range");
+        uint32_t* w = nullptr;
+        rc = zp::static_scratch(dev, &w);
+        if (rc != ZERO_OK) return rc;
+        int cu_count = 0;
+        e = hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return zp::fail_hip(e, "hipDeviceGetAttribute");
+        // one call at a time per device in this process: the calls share the
+        // device's scratch words
+        std::lock_guard<std::mutex> lock(zp::g_noalloc_mu[dev]);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        // the flag, the counter and the decision word start at 0
+        e = hipMemsetAsync(w, 0, zp::kStaticScratchWords * sizeof(uint32_t), s);
+        if (e != hipSuccess) return zp::fail_hip(e, "hipMemsetAsync (scratch)");
+
+        zp::StepLaunch a;
+        std::memset(&a, 0, sizeof(a));
+        for (int r = 0; r < R; ++r) a.grad[r] = grads[r];
+        a.R = R;
+        zp::step_constants(&a, st, pingpong, hp, sc, out_slot, S);
+        a.flag = w;
+        a.epoch = 1;
+        a.done = reinterpret_cast<unsigned long long*>(w + 16);
+        a.host_word = reinterpret_cast<unsigned long long*>(w + 32);
+        const zp::KernelEvents none;
+        if (pingpong) {
+            e = zp::launch_fused_step(a, s, none);
+            if (e != hipSuccess) return zp::fail_hip(e, "shard step kernel launch");
+        } else {
+            e = zp::launch_check(a, cu_count, s, nullptr);
+            if (e != hipSuccess) return zp::fail_hip(e, "check kernel launch");
+            e = zp::launch_update_in_place(a, s, nullptr);
+            if (e != hipSuccess) return zp::fail_hip(e, "update kernel launch");
+        }
+        unsigned long long word = 0;
+        e = hipMemcpyAsync(&word, a.host_word, sizeof(word), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return zp::fail_hip(e, "reading the overflow decision");
+        if ((word >> 1) != 1ull)
+            return fail(ZERO_ERR_STATE, "the pass ended without writing the overflow decision");
+        flag = int32_t(word & 1ull);
+        if (flag && pingpong) {
+            // the pass wrote the slot speculatively; restore fp16(master)
+            e = zp::launch_slot_from_master(a, cu_count, s);
             if (e != hipSuccess) return zp::fail_hip(e, "slot restore kernel launch");
         }
     }
@@ -473,7 +556,8 @@ extern "C" int zero_owner_step(const zero_layout* layout, int32_t rank, zero_sha
         rc = zp::begin_step(stream, "zero_owner_step", &ws, &lock, &dev);
         if (rc != ZERO_OK) return rc;
         hipStream_t s = static_cast<hipStream_t>(stream);
-        zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, S, ws);
+        zp::step_constants(&a.st, st, pingpong, hp, sc, out_slot, S);
+        zp::workspace_words(&a.st, ws);
         a.st.R = a.R;
 
         zp::KernelEvents ev;

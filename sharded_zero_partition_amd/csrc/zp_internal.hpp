@@ -169,4 +169,10 @@ void timing_done();
 // slot restore), read once from ZERO_BLOCKS_PER_CU when set.
 int blocks_per_cu_step();
 
+// The fixed scratch of zero_shard_step_noalloc (noalloc.hip): 64 words, 256
+// bytes, one copy per device.  static_scratch returns device `dev`'s address
+// of it (looked up once per device, with `dev` the current device).
+constexpr int kStaticScratchWords = 64;
+int static_scratch(int dev, uint32_t** out);
+
 }  // namespace zp

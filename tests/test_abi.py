@@ -175,6 +175,17 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(sc=zp.LossScaler.make(1024.0, min_scale=0.0)) == -1
     assert call(sc=zp.LossScaler.make(1024.0, min_scale=2.0 ** -25)) == -1
     assert b"2^-24" in zp.lib.zero_last_error()
+    st_big = zp.ShardStateC.from_buffer_copy(st)
+    st_big.shard_elems = 4096 * (2 ** 31 - 1) + 1                   # above ZERO_MAX_SHARD_ELEMS
+    assert call(st=st_big) == -1 and b"ZERO_MAX_SHARD_ELEMS" in zp.lib.zero_last_error()
+    # the no-allocation variant takes the same checks before any HIP call
+    noalloc = lambda st=st, sc=sc: zp.lib.zero_shard_step_noalloc(  # noqa: E731
+        ctypes.byref(st), grads, 2, ctypes.byref(hp), ctypes.byref(sc), slot, None, ctypes.byref(flag))
+    assert noalloc(st=st_big) == -1
+    assert noalloc(sc=zp.LossScaler.make(1024.0, min_scale=0.0)) == -1
+    st_mis = zp.ShardStateC.from_buffer_copy(st)
+    st_mis.p[0] = base + 8
+    assert noalloc(st=st_mis) == -2
     assert call(slot=ctypes.c_void_p(base + 24577)) == -2             # slot odd address
     assert call(g=(ctypes.c_void_p * 2)(base + 16386, base + 20480)) == -2
     assert call(g=(ctypes.c_void_p * 2)(None, base + 20480)) == -1
