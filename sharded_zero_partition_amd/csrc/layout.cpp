@@ -49,6 +49,7 @@ struct zero_layout {
     int64_t* d_rlen = nullptr;
     const uint16_t** d_rptr = nullptr;
     int32_t* d_rfirst = nullptr;
+    uint8_t* d_rrec = nullptr;   // per-chunk records (zp::chunk_rec_bytes(R) each)
     // host copy of the contribution tensors' byte ranges, sorted by start,
     // with the running maximum of their ends (overlap queries)
     std::vector<uintptr_t> r_start, r_end_max;
@@ -71,13 +72,14 @@ void free_device_tables(zero_layout* l) {
 }
 
 void free_reduce_tables(zero_layout* l) {
-    void* bufs[4] = {l->d_roff, l->d_rlen, l->d_rptr, l->d_rfirst};
+    void* bufs[5] = {l->d_roff, l->d_rlen, l->d_rptr, l->d_rfirst, l->d_rrec};
     for (void* b : bufs)
         if (b) (void)hipFree(b);
     l->d_roff = nullptr;
     l->d_rlen = nullptr;
     l->d_rptr = nullptr;
     l->d_rfirst = nullptr;
+    l->d_rrec = nullptr;
     l->r_device = -1;
     l->r_ranks = 0;
     l->r_nsrc = 0;
@@ -487,6 +489,31 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "too many tensors");
     if (!chunk_index(offs, l->psi, &shift, &first))
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    // Per-chunk records: for chunk c, the entries of tensor first[c] (flat
+    // offset, length, index, and its R addresses) in one place, so a wave
+    // reads everything about the tensor holding its first element with one
+    // set of loads from one address.
+    const size_t n_chunks = first.size() - 1;
+    const size_t rec_bytes = size_t(zp::chunk_rec_bytes(R));
+    std::vector<uint8_t> recs;
+    try {
+        recs.assign(std::max<size_t>(1, n_chunks) * rec_bytes, 0);
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
+    for (size_t c = 0; c < n_chunks; ++c) {
+        const size_t si = size_t(first[c]);
+        uint8_t* rec = recs.data() + c * rec_bytes;
+        const int64_t off = offs[si], len = lens[si];
+        const int32_t idx = first[c];
+        std::memcpy(rec + 0, &off, 8);
+        std::memcpy(rec + 8, &len, 8);
+        std::memcpy(rec + 16, &idx, 4);
+        for (int32_t r = 0; r < R; ++r) {
+            const uint16_t* p = ptrs[size_t(r) * offs.size() + si];
+            std::memcpy(rec + 24 + 8 * size_t(r), &p, 8);
+        }
+    }
     std::vector<uintptr_t> starts, end_max;
     try {
         std::vector<std::pair<uintptr_t, uintptr_t>> rg;
@@ -514,16 +541,17 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     const int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_contributions");
     if (rc != ZERO_OK) return rc;
     const size_t n = std::max<size_t>(1, offs.size());
-    void* d[4] = {nullptr, nullptr, nullptr, nullptr};
-    const size_t bytes[4] = {n * sizeof(int64_t), n * sizeof(int64_t),
+    void* d[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+    const size_t bytes[5] = {n * sizeof(int64_t), n * sizeof(int64_t),
                              std::max<size_t>(1, ptrs.size()) * sizeof(void*),
-                             first.size() * sizeof(int32_t)};
-    for (int k = 0; k < 4 && e == hipSuccess; ++k) e = hipMalloc(&d[k], bytes[k]);
+                             first.size() * sizeof(int32_t), recs.size()};
+    for (int k = 0; k < 5 && e == hipSuccess; ++k) e = hipMalloc(&d[k], bytes[k]);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const void* host[4] = {offs.data(), lens.data(), ptrs.data(), first.data()};
-    const size_t used[4] = {offs.size() * sizeof(int64_t), lens.size() * sizeof(int64_t),
-                            ptrs.size() * sizeof(void*), first.size() * sizeof(int32_t)};
-    for (int k = 0; k < 4 && e == hipSuccess; ++k)
+    const void* host[5] = {offs.data(), lens.data(), ptrs.data(), first.data(), recs.data()};
+    const size_t used[5] = {offs.size() * sizeof(int64_t), lens.size() * sizeof(int64_t),
+                            ptrs.size() * sizeof(void*), first.size() * sizeof(int32_t),
+                            n_chunks * rec_bytes};
+    for (int k = 0; k < 5 && e == hipSuccess; ++k)
         if (used[k]) e = hipMemcpyAsync(d[k], host[k], used[k], hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
@@ -536,6 +564,7 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     l->d_rlen = static_cast<int64_t*>(d[1]);
     l->d_rptr = static_cast<const uint16_t**>(d[2]);
     l->d_rfirst = static_cast<int32_t*>(d[3]);
+    l->d_rrec = static_cast<uint8_t*>(d[4]);
     l->r_ranks = R;
     l->r_nsrc = int32_t(offs.size());
     l->r_shift = shift;
@@ -559,6 +588,7 @@ int owner_tables(const zero_layout* l, int32_t rank, ReduceLaunch* out, int* bou
     a.len = l->d_rlen;
     a.ptr = l->d_rptr;
     a.first = l->d_rfirst;
+    a.rec = l->d_rrec;
     a.n_src = l->r_nsrc;
     a.chunk_shift = l->r_shift;
     a.R = l->r_ranks;
@@ -613,6 +643,7 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     a.len = l->d_rlen;
     a.ptr = l->d_rptr;
     a.first = l->d_rfirst;
+    a.rec = l->d_rrec;
     a.n_src = l->r_nsrc;
     a.chunk_shift = l->r_shift;
     a.R = l->r_ranks;

@@ -127,6 +127,12 @@ struct ToShard {
     __device__ static void elem(const Launch& a, int64_t j, float s, bool&) {
         a.shard[j] = uint16_t(f2h(s));
     }
+    // the elements of the vector at jv whose bit is set in mask
+    __device__ static void part(const Launch& a, int64_t jv, const float s[8], unsigned mask, bool&) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((mask >> e) & 1) a.shard[jv + e] = uint16_t(f2h(s[e]));
+    }
     __device__ static void finish(const Launch&, bool) {}
 };
 
@@ -265,6 +271,29 @@ struct ToAdam {
         c.v_out[j] = v;
         c.out16[j] = uint16_t(f2h(p));
     }
+    // the elements of the vector at jv whose bit is set in mask, every load
+    // issued before the first is used
+    __device__ static void part(const Launch& a, int64_t jv, const float s[8], unsigned mask, bool& bad) {
+        const StepLaunch& c = a.st;
+        float p[8], m[8], v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool in = (mask >> e) & 1;
+            p[e] = in ? c.p_in[jv + e] : 0.0f;
+            m[e] = in ? c.m_in[jv + e] : 0.0f;
+            v[e] = in ? c.v_in[jv + e] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (!((mask >> e) & 1)) continue;
+            bad |= not_finite(s[e]);
+            adam_element(c, s[e], p[e], m[e], v[e]);
+            c.p_out[jv + e] = p[e];
+            c.m_out[jv + e] = m[e];
+            c.v_out[jv + e] = v[e];
+            c.out16[jv + e] = uint16_t(f2h(p[e]));
+        }
+    }
     __device__ static void finish(const Launch& a, bool bad) {
         const unsigned long long ballot = __ballot(bad);
         if (ballot != 0ull && (threadIdx.x & 63) == 0) atomicMax(a.st.flag, a.st.epoch);
@@ -279,7 +308,7 @@ struct ToAdam {
 constexpr int kGroup = 4;
 
 template <int R, class Epi>
-__device__ __forceinline__ void coop_span(const typename Epi::Launch& a, int src, int64_t rel0,
+__device__ __forceinline__ void coop_span(const typename Epi::Launch& a, const uint16_t* const (&src)[R], int64_t rel0,
                                           int64_t kw, int mis, int lane, bool& bad,
                                           const typename Epi::SpanPre& pre) {
     constexpr int G = R < kGroup ? R : kGroup;
@@ -294,7 +323,7 @@ __device__ __forceinline__ void coop_span(const typename Epi::Launch& a, int src
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             if (r0 + j >= R) break;
-            const uint16_t* t = a.ptr[int64_t(r0 + j) * a.n_src + src];
+            const uint16_t* t = src[r0 + j];
             const uint16_t* p0 = t + rel0;
             ph[j] = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
             const uint16_t* b0 = p0 - ph[j] + dep;
@@ -326,6 +355,139 @@ __device__ __forceinline__ void coop_span(const typename Epi::Launch& a, int src
     Epi::span_done(a, j0, s, pre, lane, bad);
 }
 
+// Spans off the cooperative path: spans that hold tensor boundaries, and
+// spans at the ends of the owner's range.  Their elements used to wait on a
+// chain of dependent reads each (a binary search over the table, the
+// tensor's entry, its address, then the data, one element after another); a
+// wave like that lives many times longer than the others, and as the last
+// wave of a launch it holds up the launch's end.  So the span's candidate
+// tensors (at most kStage of them) are staged first: lane l reads the start,
+// end and R addresses of tensor lo + l into the wave's LDS slice, all at
+// once.  Each vector then finds its tensor in LDS; a vector inside one tensor
+// reads aligned blocks, and any other vector finds each element's tensor in
+// LDS and issues all eight elements' loads of a contribution together.
+// One per-chunk record of the reduce tables (layout: chunk_rec_bytes).
+template <int R>
+struct alignas(16) ChunkRec {
+    int64_t off;
+    int64_t len;
+    int32_t idx;
+    int32_t pad;
+    const uint16_t* ptr[R];
+};
+static_assert(sizeof(ChunkRec<1>) == chunk_rec_bytes(1) && sizeof(ChunkRec<2>) == chunk_rec_bytes(2) &&
+                  sizeof(ChunkRec<5>) == chunk_rec_bytes(5) && sizeof(ChunkRec<16>) == chunk_rec_bytes(16),
+              "record layout");
+
+template <int R>
+struct Stage {
+    static constexpr int kMax = R <= 4 ? 64 : 16;   // candidate tensors per span
+    int64_t off[kMax];
+    int64_t end[kMax];
+    const uint16_t* ptr[R][kMax];
+};
+
+template <int R, class Epi>
+__device__ __forceinline__ void staged_vectors(const typename Epi::Launch& a, int lo, int ncand, int64_t kw,
+                                               int64_t k_end, int mis, int64_t j_lo, int64_t j_hi, int lane,
+                                               int wave_in_block, bool& bad) {
+    __shared__ Stage<R> stage[kThreads / 64];
+    Stage<R>& st = stage[wave_in_block];
+    if (lane < ncand) {
+        const int64_t o = a.off[lo + lane];
+        st.off[lane] = o;
+        st.end[lane] = o + a.len[lo + lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) st.ptr[r][lane] = a.ptr[int64_t(r) * a.n_src + lo + lane];
+    }
+    // only this wave touches its slice: LDS operations of one wave complete
+    // in order, the fences keep the compiler from reordering
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+    for (int u = 0; u < kU; ++u) {
+        const int64_t k = kw + 64 * u + lane;
+        if (k >= k_end) continue;
+        const int64_t jv = k * 8 - mis;
+        const int64_t g0 = a.base + jv;
+        // the candidate holding g0 (the span's first in-range position is in
+        // candidate 0, so g0 < off[0] only for a vector that starts before
+        // the range, whose elements there are not read)
+        int i0 = 0;
+        for (int step = Stage<R>::kMax / 2; step > 0; step >>= 1)   // binary search in LDS
+            if (i0 + step < ncand && st.off[i0 + step] <= g0) i0 += step;
+        const bool whole = jv >= j_lo && jv + 8 <= j_hi;
+        if (whole && g0 >= st.off[i0] && g0 + 8 <= st.end[i0]) {
+            const int64_t soff = st.off[i0];
+            const int64_t slen = st.end[i0] - soff;
+            const int64_t rel = g0 - soff;
+            typename Epi::Pre pre;
+            Epi::pre(a, jv, pre);
+            float s[8];
+            int64_t dep = 0;   // as in coop_span: groups of kGroup contributions
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint16_t* t = st.ptr[r][i0] + dep;
+                const u32x4 v = load8(t + rel, t, t + slen);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = h2f(w[e >> 1] >> (16 * (e & 1)));
+                    s[e] = r == 0 ? x : s[e] + x;
+                }
+                if ((r + 1) % kGroup == 0 && r + 1 < R) asm volatile("" : "+v"(dep) : "v"(s[0]));
+            }
+            Epi::vec(a, jv, s, pre, bad);
+            continue;
+        }
+        // across boundaries or at a range end: each element's candidate from
+        // LDS, then per contribution all eight elements' loads at once
+        unsigned mask = 0;
+        int cand[8];
+        int ie = i0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            while (ie + 1 < ncand && st.off[ie + 1] <= g0 + e) ++ie;
+            cand[e] = ie;
+            if (jv + e >= j_lo && jv + e < j_hi) mask |= 1u << e;
+        }
+        int64_t rel[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rel[e] = g0 + e - st.off[cand[e]];
+        // contributions in groups of kGroup, each group's loads all issued
+        // before any is used; the sums carry over in contribution order
+        constexpr int G = R < kGroup ? R : kGroup;
+        float s[8];
+        int64_t dep = 0;   // as in coop_span: the next group waits for this one's sums
+#pragma unroll
+        for (int r0 = 0; r0 < R; r0 += G) {
+            uint32_t x[G][8];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (r0 + j >= R) break;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[j][e] = (mask >> e) & 1 ? ld2(st.ptr[r0 + j][cand[e]] + rel[e] + dep) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (r0 + j >= R) break;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] = r0 + j == 0 ? h2f(x[j][e]) : s[e] + h2f(x[j][e]);
+            }
+            if (r0 + G < R) asm volatile("" : "+v"(dep) : "v"(s[0]));
+        }
+        if (mask == 0xFFu) {
+            typename Epi::Pre pre;
+            Epi::pre(a, jv, pre);
+            Epi::vec(a, jv, s, pre, bad);
+        } else {
+            Epi::part(a, jv, s, mask, bad);
+        }
+    }
+}
+
 template <int R, class Epi>
 __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     constexpr int nr = R;   // contributions (compile-time: every loop over them unrolls)
@@ -353,14 +515,27 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     const int64_t k_last = min(kw + kSpanVec, k_end) - 1;
     const int64_t jf = max(kw * 8 - mis, j_lo);
     const int64_t jl = min(k_last * 8 - mis + 8, j_hi) - 1;
-    const int lo = a.first[(a.base + jf) >> a.chunk_shift];
+    // The record of the chunk holding the span's first position carries the
+    // entries of the tensor holding that chunk's start (offset, length, index
+    // and R addresses), and the chunk index gives the last candidate: two
+    // independent reads, so the tables cost one latency before the data
+    // loads.  (A chain of table reads -- chunk index, then the tensor's
+    // entries, then its addresses -- meets cold lines at the start and the
+    // end of every launch and added a few microseconds to each.)
+    const ChunkRec<R>& rec = reinterpret_cast<const ChunkRec<R>*>(a.rec)[(a.base + jf) >> a.chunk_shift];
     const int hi = a.first[((a.base + jl) >> a.chunk_shift) + 1];
+    const int lo = rec.idx;
+    const int64_t one_off = rec.off;
+    const int64_t one_len = rec.len;
+    const uint16_t* one_ptr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) one_ptr[r] = rec.ptr[r];
+    // keeps the compiler from sinking the address loads into the branches
+    // below, behind a second wait (after every load: a load placed after
+    // such a statement could no longer go through the scalar cache)
+#pragma unroll
+    for (int r = 0; r < R; ++r) asm volatile("" ::"s"(one_ptr[r]));
     const bool one = lo == hi;
-    int64_t one_off = 0, one_len = 0;
-    if (one) {
-        one_off = a.off[lo];
-        one_len = a.len[lo];
-    }
 
     // Cooperative path: a span of full vectors inside one tensor has one
     // misalignment phase per contribution for the whole wave, so each lane
@@ -371,7 +546,7 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
         const int64_t rel0 = a.base + kw * 8 - mis - one_off;    // >= 0, span inside the tensor
         bool in_bounds = true;
         for (int r = 0; r < nr; ++r) {
-            const uint16_t* t = a.ptr[int64_t(r) * a.n_src + lo];
+            const uint16_t* t = one_ptr[r];
             const uint16_t* p0 = t + rel0;
             const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
             const uint16_t* b0 = p0 - ph;
@@ -380,10 +555,16 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
         }
         if (in_bounds) {
             // every contribution's loads are issued before the first shuffle
-            coop_span<R, Epi>(a, lo, rel0, kw, mis, lane, bad, pre);
+            coop_span<R, Epi>(a, one_ptr, rel0, kw, mis, lane, bad, pre);
             Epi::finish(a, bad);
             return;
         }
+    }
+
+    if (hi - lo < Stage<R>::kMax) {
+        staged_vectors<R, Epi>(a, lo, hi - lo + 1, kw, k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
+        Epi::finish(a, bad);
+        return;
     }
 
 #pragma unroll

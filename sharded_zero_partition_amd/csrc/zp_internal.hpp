@@ -56,11 +56,18 @@ hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEven
 
 constexpr int kMaxReduceRanks = 16;
 
+// Bytes of one per-chunk record of the reduce tables for R contributions:
+// int64 flat offset (byte 0), int64 length (8), int32 tensor index (16), 4
+// bytes padding, then R device addresses (24 + 8 r); rounded up to 16.
+constexpr int chunk_rec_bytes(int R) { return (24 + 8 * R + 15) / 16 * 16; }
+
 struct ReduceLaunch {
     const int64_t* off;          // device, n_src flat offsets (sorted)
     const int64_t* len;          // device, n_src lengths (> 0)
     const uint16_t* const* ptr;  // device, R * n_src addresses, row r = rank r
     const int32_t* first;        // device chunk index, as in PackLaunch
+    const uint8_t* rec;          // device, one chunk_rec_bytes(R) record per chunk c:
+                                 // the entries of tensor first[c]
     int32_t n_src;
     int32_t chunk_shift;
     int32_t R;

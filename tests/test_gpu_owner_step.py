@@ -179,6 +179,29 @@ def test_seeded_random_cases():
         lay.close()
 
 
+@pytest.mark.parametrize("R", [2, 7])
+def test_runs_of_tiny_tensors(R):
+    """Owner steps over layouts with runs of 1..9-element tensors between
+    longer ones (spans with dozens, and with more than 64, tensor
+    boundaries), every rank, two steps."""
+    rng = np.random.default_rng(600 + R)
+    numels = []
+    for _ in range(10):
+        numels += [int(x) for x in rng.integers(1, 10, size=int(rng.choice([5, 40, 120])))]
+        numels.append(int(rng.choice([700, 3000, 9000])))
+    lay = zp.partition_layout(numels, 3, stage=2, align=8, bucket=1 << 13)
+    olay = OL.partition_layout(numels, 3, 2, 8, 1 << 13)
+    bufs, lists = _lists(rng, numels, R)
+    lay.bind_contributions(lists)
+    runs = [OwnerRun(olay, r, rng, slot_offset=int(rng.integers(0, 8))) for r in range(3)]
+    for step in range(2):
+        host = _host(lists)
+        for r, run in enumerate(runs):
+            assert run.step(lay, r, host) == 0
+        _redraw(rng, bufs)
+    lay.close()
+
+
 def test_every_finite_fp16_class():
     """Contributions drawn as random fp16 bit patterns with a finite
     exponent: subnormals, signed zeros and values up to 65504 (16 of them sum

@@ -69,6 +69,48 @@ def test_small_all_fills_and_owners(R):
             assert (h[:mis] == SENT).all() and (h[mis + S:] == SENT).all()
 
 
+@pytest.mark.parametrize("R", [1, 2, 5, 16])
+def test_runs_of_tiny_tensors(R):
+    """Spans that hold many tensor boundaries: runs of 1..9-element tensors
+    (more than 64 tensors in one 1024-element span, and runs of a few dozen)
+    between longer tensors, so that the staged path for spans with up to 64
+    candidate tensors and the path beyond it both run, across misaligned
+    sources and shard bases; every fill and owner against the oracle."""
+    rng = np.random.default_rng(300 + R)
+    for trial in range(3):
+        numels = []
+        for _ in range(12):
+            numels += [int(x) for x in rng.integers(1, 10, size=int(rng.choice([3, 20, 60, 150])))]
+            numels.append(int(rng.choice([100, 1500, 5000, 20000])))
+        n_ranks = int(rng.integers(1, 5))
+        bucket = int(rng.choice([4096, 1 << 14, 1 << 16]))
+        lay = zp.partition_layout(numels, n_ranks, stage=2, align=8, bucket=bucket)
+        olay = OL.partition_layout(numels, n_ranks, 2, 8, bucket)
+        lists = _lists(rng, numels, R)
+        lay.bind_contributions(lists)
+        host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+        S = olay.shard
+        print(f"[tiny runs] R={R} trial={trial} tensors={len(numels)} psi={olay.psi} ranks={n_ranks} "
+              f"fills={olay.n_fills}", flush=True)
+        for r in range(n_ranks):
+            mis = int(rng.integers(0, 8))
+            holder = torch.full((S + 16,), SENT, dtype=torch.int16, device="cuda")
+            shard = holder[mis:mis + S]
+            want = np.full(S, SENT, np.uint16)
+            for k in range(olay.n_fills):
+                n = lay.reduce_to_owner(k, r, shard)
+                off, vals = oracle.reduce_to_owner(host, olay, k, r)
+                assert n == vals.size
+                want[off:off + vals.size] = vals
+            got = shard.cpu().numpy().view(np.uint16)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                raise AssertionError(f"trial {trial} rank {r}: {bad.size} differ, first {bad[0]}")
+            h = holder.cpu().numpy().view(np.uint16)
+            assert (h[:mis] == SENT).all() and (h[mis + S:] == SENT).all()
+        lay.close()
+
+
 def test_errors():
     numels = [10, 20]
     lay = zp.partition_layout(numels, 2, bucket=16)
