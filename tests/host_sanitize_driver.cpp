@@ -2,9 +2,10 @@
 // and the scalar C oracle, built with AddressSanitizer and
 // UndefinedBehaviorSanitizer and driven without a device.
 //
-// The kernel launch functions live in the .hip sources, which the sanitized build
-// leaves out: the stubs below stand in for them and fail if reached, since
-// nothing here may launch.  The driver exercises
+// The kernel launch functions and the device scratch of the no-allocation
+// step live in the .hip sources, which the sanitized build leaves out: the
+// stubs below stand in for them and fail if reached, since nothing here may
+// launch.  The driver exercises
 //   - partition layouts of seeded random tensor lists: info, offsets, rank
 //     ranges, all three segment queries with their sizing protocol, arena
 //     plans for every stage, with invariants checked on the way;
@@ -34,6 +35,10 @@ hipError_t launch_check(const StepLaunch&, int, hipStream_t, hipEvent_t) { retur
 hipError_t launch_update_in_place(const StepLaunch&, hipStream_t, hipEvent_t) { return never("update"); }
 hipError_t launch_slot_from_master(const StepLaunch&, int, hipStream_t) { return never("slot"); }
 hipError_t launch_owner_step(const OwnerLaunch&, hipStream_t, const KernelEvents&) { return never("owner"); }
+int static_scratch(int, uint32_t**) {
+    (void)never("static scratch");
+    return -1;
+}
 }  // namespace zp
 
 extern "C" {
@@ -180,6 +185,21 @@ static void argument_errors() {
     zero_shard_state st2 = st;
     st2.p[0] = reinterpret_cast<float*>(base + 8);
     CHECK(zero_shard_step(&st2, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_ALIGNMENT);
+    // the loss-scale floor and the largest shard
+    bad_sc = sc;
+    bad_sc.min_scale = 0.0f;
+    CHECK(zero_shard_step(&st, grads, 2, &hp, &bad_sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    bad_sc = sc;
+    bad_sc.scale = ZERO_MIN_LOSS_SCALE / 2;
+    CHECK(zero_shard_step(&st, grads, 2, &hp, &bad_sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    zero_shard_state huge = st;
+    huge.shard_elems = ZERO_MAX_SHARD_ELEMS + 1;
+    CHECK(zero_shard_step(&huge, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    // the no-allocation variant runs the same checks before any HIP call
+    CHECK(zero_shard_step_noalloc(&st, grads, 0, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_shard_step_noalloc(&huge, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
+    CHECK(zero_shard_step_noalloc(&st2, grads, 2, &hp, &sc, slot, nullptr, &flag) == ZERO_ERR_ALIGNMENT);
+    CHECK(zero_shard_step_noalloc(&st, grads, 2, &hp, &bad_sc, slot, nullptr, &flag) == ZERO_ERR_INVALID_ARG);
     CHECK(sc.scale == 1024.0f && st.t == 0 && flag == -1);
 
     // owner step and reduce-to-owner: unbound and out-of-range arguments
