@@ -151,6 +151,12 @@ def _load():
     return lib
 
 
+# torch brings its own copy of the HIP runtime (same soname).  Importing torch
+# first makes this library bind to that copy, so one runtime serves both;
+# loaded the other way round, a process would hold two runtimes, and the
+# second one initialised can find no device.
+import torch  # noqa: E402,F401
+
 lib = _load()
 
 

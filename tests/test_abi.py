@@ -336,3 +336,18 @@ def test_arena_plan_errors(zp):
         with pytest.raises(zp.ZeroError, match="INVALID_ARG"):
             lay.arena_plan(**bad)
     assert lay.arena_plan().align_bytes == 1 << 21
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """torch ships its own copy of the HIP runtime under the same soname.  The
+    binding imports torch before it loads the library, so a process that
+    imports the package first still maps one runtime, not two."""
+    import subprocess
+    import sys
+    code = ("import sharded_zero_partition_amd as zp\n"
+            "zp.version()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, check=True)
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout + out.stderr
