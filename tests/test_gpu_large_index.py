@@ -34,8 +34,10 @@ def test_shard_step_past_2_31():
     S = w.shard
     assert S == B31 + 4099
     rng = np.random.default_rng(31)
+    tiles = np.arange(0, S, 1024, dtype=np.int64)           # one element of every 1024-element tile
     idx = np.concatenate([np.arange(8192), np.arange(B31 - 8192, B31 + 4099),
-                          rng.integers(0, S, size=200_000)])
+                          rng.integers(0, S, size=200_000),
+                          np.minimum(tiles + rng.integers(0, 1024, size=tiles.size), S - 1)])
     sample = np.unique(idx).astype(np.int64)
     print(f"[past_2_31] S={S} R={w.n_contrib} steps={w.steps} sample={sample.size}", flush=True)
     p0 = W.master_init(w, device="cuda")

@@ -413,7 +413,8 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     """R whole gradient streams (workloads.gradient_stream), the owner step of
     `rank` for `steps` steps with new streams each step, compared on a sample
     of the rank's shard (both ends of its real range, every tensor boundary
-    inside it, n_sample random positions and all of its padding) against the
+    inside it, one random element of every 1024-element tile, n_sample random
+    positions and all of its padding) against the
     oracle's shard step over the sampled sums (zero over the padding).  The draws are finite and their
     pairwise fp32 sums cannot overflow, so the overflow flag is 0 unless
     `plant` ({step: [(contribution, flat index, fp16 bits)]}) puts a special
@@ -428,9 +429,11 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     rng = np.random.default_rng(wid * 100 + rank)
     inner = offs[(offs > lo) & (offs < lo + n)] - lo
     planted = [g - lo for v in (plant or {}).values() for _, g, _ in v if lo <= g < lo + n]
+    tiles = np.arange(0, n, 1024, dtype=np.int64)           # one element of every 1024-element tile
     pick = np.concatenate([np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n),
                            inner, inner - 1, rng.integers(0, max(n, 1), size=n_sample),
-                           np.asarray(planted, np.int64), np.arange(n, S)])
+                           np.asarray(planted, np.int64), np.arange(n, S),
+                           tiles + rng.integers(0, 1024, size=tiles.size)])
     sample = np.unique(pick[(pick >= 0) & (pick < S)]).astype(np.int64)
     real = sample < n
     g = sample[real] + lo
