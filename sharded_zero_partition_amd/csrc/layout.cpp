@@ -37,7 +37,6 @@ struct zero_layout {
     int device = -1;
     zp::PackSrc* d_src = nullptr;
     int32_t* d_first = nullptr;
-    zp::PackRec* d_prec = nullptr;   // per-chunk records
     int32_t n_src = 0;
     int32_t chunk_shift = 0;
 
@@ -66,10 +65,8 @@ bool add_overflows(int64_t a, int64_t b) { return a > kI64Max - b; }
 void free_device_tables(zero_layout* l) {
     if (l->d_src) (void)hipFree(l->d_src);
     if (l->d_first) (void)hipFree(l->d_first);
-    if (l->d_prec) (void)hipFree(l->d_prec);
     l->d_src = nullptr;
     l->d_first = nullptr;
-    l->d_prec = nullptr;
     l->device = -1;
     l->n_src = 0;
 }
@@ -376,16 +373,6 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     }
     if (!chunk_index(offs, l->psi, &shift, &first))
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
-    // per-chunk records: a wave reads the entry of the tensor holding its
-    // chunk's start in one load, independent of the chunk index
-    const size_t n_chunks = first.size() - 1;
-    std::vector<zp::PackRec> recs;
-    try {
-        recs.resize(std::max<size_t>(1, n_chunks));
-    } catch (...) {
-        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
-    }
-    for (size_t c = 0; c < n_chunks; ++c) recs[c] = {src[size_t(first[c])], first[c], 0};
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -395,37 +382,29 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
 
     zp::PackSrc* d_src = nullptr;
     int32_t* d_first = nullptr;
-    zp::PackRec* d_prec = nullptr;
     const size_t src_bytes = std::max<size_t>(1, src.size()) * sizeof(zp::PackSrc);
     const size_t first_bytes = first.size() * sizeof(int32_t);
-    const size_t rec_bytes = recs.size() * sizeof(zp::PackRec);
     e = hipMalloc(reinterpret_cast<void**>(&d_src), src_bytes);
     if (e != hipSuccess) return zp::fail_hip(e, "hipMalloc (pack sources)");
     e = hipMalloc(reinterpret_cast<void**>(&d_first), first_bytes);
-    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&d_prec), rec_bytes);
     if (e != hipSuccess) {
         (void)hipFree(d_src);
-        if (d_first) (void)hipFree(d_first);
-        return zp::fail_hip(e, "hipMalloc (pack chunk tables)");
+        return zp::fail_hip(e, "hipMalloc (pack chunk index)");
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!src.empty()) e = hipMemcpyAsync(d_src, src.data(), src.size() * sizeof(zp::PackSrc),
                                          hipMemcpyHostToDevice, st);
     if (e == hipSuccess)
         e = hipMemcpyAsync(d_first, first.data(), first_bytes, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess && n_chunks)
-        e = hipMemcpyAsync(d_prec, recs.data(), n_chunks * sizeof(zp::PackRec), hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
         (void)hipFree(d_src);
         (void)hipFree(d_first);
-        (void)hipFree(d_prec);
         return zp::fail_hip(e, "uploading pack tables");
     }
     free_device_tables(l);
     l->d_src = d_src;
     l->d_first = d_first;
-    l->d_prec = d_prec;
     l->n_src = int32_t(src.size());
     l->chunk_shift = shift;
     l->device = dev;
@@ -452,7 +431,6 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     zp::PackLaunch a;
     a.src = l->d_src;
     a.first = l->d_first;
-    a.rec = l->d_prec;
     a.n_src = l->n_src;
     a.chunk_shift = l->chunk_shift;
     a.psi = l->psi;

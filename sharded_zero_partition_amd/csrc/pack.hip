@@ -80,21 +80,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
     if (o_wave >= a.bucket_elems) return;   // the whole wave leaves together
     const int64_t g_wave = a.fill_base + o_wave;
     int lo = 0, hi = 0;
-    PackSrc uni = {nullptr, 0, 0};
     if (g_wave < a.psi) {
         int64_t g_last = a.fill_base + min(o_wave + kSpan, a.bucket_elems) - 1;
         if (g_last >= a.psi) g_last = a.psi - 1;
-        // sources of the span lie in [first[chunk(g_wave)], first[chunk(g_last) + 1]];
-        // the record of chunk(g_wave) holds the first of them and its entry,
-        // read together with the last index (one table latency)
-        const PackRec& rec = a.rec[g_wave >> a.chunk_shift];
+        // sources of the span lie in [first[chunk(g_wave)], first[chunk(g_last) + 1]]
+        lo = a.first[g_wave >> a.chunk_shift];
         hi = a.first[(g_last >> a.chunk_shift) + 1];
-        lo = rec.idx;
-        uni = rec.src;
     }
     // when the whole span lies in one tensor (the common case) its table
-    // entry is wave-uniform, in scalar registers
+    // entry is wave-uniform and read once through the scalar cache
     const bool one_src = lo == hi;
+    PackSrc uni = {nullptr, 0, 0};
+    if (one_src && g_wave < a.psi) uni = a.src[lo];
 
     // Cooperative path: a full span inside one tensor has one misalignment
     // phase for the whole wave, so each lane loads a single aligned block and

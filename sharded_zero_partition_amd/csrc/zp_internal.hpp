@@ -36,19 +36,10 @@ struct PackSrc {
     int64_t len;          // elements (> 0)
 };
 
-// Per-chunk record of the pack tables: the entry of the tensor holding the
-// chunk's first flat index, and that tensor's index.
-struct alignas(16) PackRec {
-    PackSrc src;
-    int32_t idx;
-    int32_t pad;
-};
-
 struct PackLaunch {
     const PackSrc* src;       // device, n_src entries sorted by flat_off
     const int32_t* first;     // device, n_chunks + 1 entries: src index holding
                               // flat index c << chunk_shift (last entry n_src - 1)
-    const PackRec* rec;       // device, n_chunks entries: rec[c].src = src[first[c]]
     int32_t n_src;
     int32_t chunk_shift;
     int64_t psi;
