@@ -53,6 +53,8 @@ struct zero_layout {
     // host copy of the contribution tensors' byte ranges, sorted by start,
     // with the running maximum of their ends (overlap queries)
     std::vector<uintptr_t> r_start, r_end_max;
+    // host copy of the device flat offsets (r_nsrc + 1 entries, the last psi)
+    std::vector<int64_t> r_off;
 };
 
 namespace {
@@ -85,6 +87,7 @@ void free_reduce_tables(zero_layout* l) {
     l->r_nsrc = 0;
     l->r_start.clear();
     l->r_end_max.clear();
+    l->r_off.clear();
 }
 
 // Chunk index over the flat stream: first[c] = index (among the non-empty
@@ -540,9 +543,16 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     if (e != hipSuccess) return zp::fail_hip(e, "hipGetDevice");
     const int rc = zp::check_stream_device(stream, dev, "zero_layout_bind_contributions");
     if (rc != ZERO_OK) return rc;
-    const size_t n = std::max<size_t>(1, offs.size());
+    // the offsets end with psi, the end of the last tensor (a sentinel
+    // boundary for the kernels' work order)
+    try {
+        offs.push_back(l->psi);
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
+    const size_t n = std::max<size_t>(1, lens.size());
     void* d[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
-    const size_t bytes[5] = {n * sizeof(int64_t), n * sizeof(int64_t),
+    const size_t bytes[5] = {offs.size() * sizeof(int64_t), n * sizeof(int64_t),
                              std::max<size_t>(1, ptrs.size()) * sizeof(void*),
                              first.size() * sizeof(int32_t), recs.size()};
     for (int k = 0; k < 5 && e == hipSuccess; ++k) e = hipMalloc(&d[k], bytes[k]);
@@ -566,11 +576,12 @@ extern "C" int zero_layout_bind_contributions(zero_layout* l, int32_t R,
     l->d_rfirst = static_cast<int32_t*>(d[3]);
     l->d_rrec = static_cast<uint8_t*>(d[4]);
     l->r_ranks = R;
-    l->r_nsrc = int32_t(offs.size());
+    l->r_nsrc = int32_t(lens.size());
     l->r_shift = shift;
     l->r_device = dev;
     l->r_start.swap(starts);
     l->r_end_max.swap(end_max);
+    l->r_off.swap(offs);
     return ZERO_OK;
 }
 
@@ -596,8 +607,28 @@ int owner_tables(const zero_layout* l, int32_t rank, ReduceLaunch* out, int* bou
     a.g_lo = lo;
     a.g_hi = std::max(lo, std::min(lo + l->shard, l->psi));
     a.shard = nullptr;
+    // p, m, v are 16-byte aligned: no misalignment
+    plan_reduce_waves(l->r_off.data(), int64_t(l->r_off.size()), l->r_shift, 0, &a);
     *out = a;
     return ZERO_OK;
+}
+
+void plan_reduce_waves(const int64_t* off, int64_t n_off, int chunk_shift, int mis, ReduceLaunch* a) {
+    a->n_span = 0;
+    a->n_hard = 2;
+    a->b_first = 0;
+    a->hard_per_b = int32_t((int64_t(1) << chunk_shift) / kOwnerSpanElems + 2);
+    if (a->g_hi <= a->g_lo) return;
+    const SpanGeometry g = span_geometry(a->base, a->g_lo - a->base, a->g_hi - a->base, mis);
+    a->n_span = g.n_span;
+    if (g.n_span < 3) return;   // no interior span
+    // boundaries that can claim an interior span: cs(F(1) - 7) < b < F(n_span - 1) + 8
+    const int64_t lo = ((g.span0 + kOwnerSpanElems - 7) >> chunk_shift) << chunk_shift;
+    const int64_t hi = g.span0 + kOwnerSpanElems * (g.n_span - 1) + 8;
+    const int64_t* first = std::upper_bound(off, off + n_off, lo);
+    const int64_t* last = std::lower_bound(off, off + n_off, hi);
+    a->b_first = int64_t(first - off);
+    a->n_hard = 2 + (last > first ? int64_t(last - first) : 0) * a->hard_per_b;
 }
 
 bool contributions_overlap(const zero_layout* l, uintptr_t lo, uintptr_t hi) {
@@ -651,6 +682,8 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     a.g_hi = g_hi;
     a.base = rank_lo;
     a.shard = shard;
+    zp::plan_reduce_waves(l->r_off.data(), int64_t(l->r_off.size()), l->r_shift,
+                          int((reinterpret_cast<uintptr_t>(shard) >> 1) & 7), &a);
     hipStream_t st = static_cast<hipStream_t>(stream);
     zp::KernelEvents ev;
     e = zp::timing_events(&ev);

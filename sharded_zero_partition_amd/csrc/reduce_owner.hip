@@ -488,22 +488,30 @@ __device__ __forceinline__ void staged_vectors(const typename Epi::Launch& a, in
     }
 }
 
-template <int R, class Epi>
-__device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
-    constexpr int nr = R;   // contributions (compile-time: every loop over them unrolls)
-    const int lane = threadIdx.x & 63;
-    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wave_in_block;
-    // vector k covers shard positions [8k - mis, 8k - mis + 8)
-    const int mis = Epi::mis(a);
-    bool bad = false;
-    const int64_t j_lo = a.g_lo - a.base;
-    const int64_t j_hi = a.g_hi - a.base;
-    const int64_t k_lo = (j_lo + mis) >> 3;
-    const int64_t k_end = ((j_hi - 1 + mis) >> 3) + 1;
-    const int64_t kw = k_lo + wave * kSpanVec;
-    if (kw >= k_end) return;   // the whole wave leaves together
+// The reads of a cooperative span at offset rel0 of a tensor of len
+// elements stay inside the tensor for every contribution (the blocks from
+// the aligned block holding rel0 on, plus one more when misaligned).
+template <int R>
+__device__ __forceinline__ bool coop_in_bounds(const uint16_t* const (&ptr)[R], int64_t rel0, int64_t len) {
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint16_t* t = ptr[r];
+        const uint16_t* p0 = t + rel0;
+        const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+        const uint16_t* b0 = p0 - ph;
+        const int64_t need = ph ? 8 * kSpanVec + 8 : 8 * kSpanVec;
+        ok = ok && b0 >= t && b0 + need <= t + len;
+    }
+    return ok;
+}
 
+// Any span, first vector kw: the cooperative path when the span is whole and
+// inside one tensor, else the staged or the per-vector path.
+template <int R, class Epi>
+__device__ __forceinline__ void general_span(const typename Epi::Launch& a, int64_t kw, int64_t k_end, int mis,
+                                             int64_t j_lo, int64_t j_hi, int lane, int wave_in_block, bool& bad) {
+    constexpr int nr = R;   // contributions (compile-time: every loop over them unrolls)
     // A span of full vectors starts its epilogue's own loads (p, m, v for the
     // owner step) before the table reads below: their addresses need only the
     // span's position, so their latency overlaps the dependent table reads.
@@ -544,26 +552,15 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     // from one extra block after the span).
     if (one && full_span) {
         const int64_t rel0 = a.base + kw * 8 - mis - one_off;    // >= 0, span inside the tensor
-        bool in_bounds = true;
-        for (int r = 0; r < nr; ++r) {
-            const uint16_t* t = one_ptr[r];
-            const uint16_t* p0 = t + rel0;
-            const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
-            const uint16_t* b0 = p0 - ph;
-            const int64_t need = ph ? 8 * kSpanVec + 8 : 8 * kSpanVec;
-            in_bounds = in_bounds && b0 >= t && b0 + need <= t + one_len;
-        }
-        if (in_bounds) {
+        if (coop_in_bounds<R>(one_ptr, rel0, one_len)) {
             // every contribution's loads are issued before the first shuffle
             coop_span<R, Epi>(a, one_ptr, rel0, kw, mis, lane, bad, pre);
-            Epi::finish(a, bad);
             return;
         }
     }
 
     if (hi - lo < Stage<R>::kMax) {
         staged_vectors<R, Epi>(a, lo, hi - lo + 1, kw, k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
-        Epi::finish(a, bad);
         return;
     }
 
@@ -610,6 +607,67 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
             Epi::elem(a, j, sum1<R>(a, i, g - a.off[i]), bad);
         }
     }
+}
+
+static_assert(kSpanVec == kOwnerSpanVec, "one span geometry for host and device");
+
+// The wave's work, in the order the launch plan sets (ReduceLaunch): the
+// first n_hard waves take the two ends of the range and the spans near
+// tensor boundaries, the rest one span each, leaving at once when a boundary
+// claims that span.
+template <int R, class Epi>
+__device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
+    const int lane = threadIdx.x & 63;
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = int64_t(blockIdx.x) * (kThreads / 64) + wave_in_block;
+    const int mis = Epi::mis(a);
+    const int64_t j_lo = a.g_lo - a.base;
+    const int64_t j_hi = a.g_hi - a.base;
+    const SpanGeometry geo = span_geometry(a.base, j_lo, j_hi, mis);
+    bool bad = false;
+
+    if (wave >= a.n_hard) {
+        // interior span w: whole and inside the range
+        const int64_t w = wave - a.n_hard;
+        if (w < 1 || w >= geo.n_span - 1) return;   // the whole wave leaves together
+        const int64_t kw = geo.k_lo + w * kSpanVec;
+        const int64_t f = geo.span0 + w * kOwnerSpanElems;
+        // the epilogue's own loads (p, m, v for the owner step) need only the
+        // span's position: issued first, their latency overlaps the record's
+        typename Epi::SpanPre pre;
+        Epi::span_pre(a, kw * 8 - mis, lane, pre);
+        const ChunkRec<R>& rec = reinterpret_cast<const ChunkRec<R>*>(a.rec)[(f - 7) >> a.chunk_shift];
+        const int64_t one_off = rec.off;
+        const int64_t one_len = rec.len;
+        const uint16_t* one_ptr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) one_ptr[r] = rec.ptr[r];
+        // keeps the address loads together, ahead of the branches below
+#pragma unroll
+        for (int r = 0; r < R; ++r) asm volatile("" ::"s"(one_ptr[r]));
+        if (span_claimed(one_off, one_len, f)) return;   // a hard wave's span
+        const int64_t rel0 = f - one_off;   // >= 7: the record's tensor starts by f - 7
+        if (coop_in_bounds<R>(one_ptr, rel0, one_len)) {
+            coop_span<R, Epi>(a, one_ptr, rel0, kw, mis, lane, bad, pre);
+        } else {
+            // Not reached (an unclaimed span lies inside the record's tensor,
+            // with 7 elements before it and 8 after it); kept so that no read
+            // can leave a tensor: element by element, each found by search.
+#pragma unroll 1
+            for (int e = 0; e < int(kOwnerSpanElems / 64); ++e) {
+                const int64_t j = kw * 8 - mis + 64 * e + lane;
+                const int64_t g = a.base + j;
+                const int i = search(a.off, 0, a.n_src - 1, g);
+                Epi::elem(a, j, sum1<R>(a, i, g - a.off[i]), bad);
+            }
+        }
+        Epi::finish(a, bad);
+        return;
+    }
+
+    const int64_t w = hard_wave_span(a, geo, a.off, wave);
+    if (w < 0) return;
+    general_span<R, Epi>(a, geo.k_lo + w * kSpanVec, geo.k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
     Epi::finish(a, bad);
 }
 
@@ -647,11 +705,9 @@ __global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsign
     __hip_atomic_store(host_word, word, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Workgroups for the vectors of shard positions [j_lo, j_hi) on a grid
-// shifted by mis elements.
-dim3 span_grid(int64_t j_lo, int64_t j_hi, int mis) {
-    const int64_t nvec = ((j_hi - 1 + mis) >> 3) + 1 - ((j_lo + mis) >> 3);
-    const int64_t waves = (nvec + kSpanVec - 1) / kSpanVec;
+// Workgroups of the launch plan: n_hard waves, then one wave per span.
+dim3 plan_grid(const ReduceLaunch& a) {
+    const int64_t waves = a.n_hard + a.n_span;
     int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
     if (blocks < 1) blocks = 1;
     return dim3{unsigned(blocks)};
@@ -660,8 +716,7 @@ dim3 span_grid(int64_t j_lo, int64_t j_hi, int mis) {
 }  // namespace
 
 hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev) {
-    const int mis = int((reinterpret_cast<uintptr_t>(a.shard) >> 1) & 7);
-    const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, mis);
+    const dim3 grid = plan_grid(a);
     switch (a.R) {
         case 1: hipExtLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
         case 2: hipExtLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
@@ -687,7 +742,7 @@ namespace {
 
 // The owner step's main pass over the real elements [g_lo, g_hi).
 void launch_owner_real(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
-    const dim3 grid = span_grid(a.g_lo - a.base, a.g_hi - a.base, 0);
+    const dim3 grid = plan_grid(a);
     switch (a.R) {
         case 1: hipExtLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
         case 2: hipExtLaunchKernelGGL(owner_step_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;

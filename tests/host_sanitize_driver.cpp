@@ -11,13 +11,18 @@
 //     plans for every stage, with invariants checked on the way;
 //   - argument errors of every entry point that can be called without a
 //     device, with fake (never dereferenced) device addresses;
-//   - the oracle's conversions, reduce, flag and Adam on random data.
+//   - the oracle's conversions, reduce, flag and Adam on random data;
+//   - the work order of the reduce-to-owner and owner-step launches (the
+//     same host/device functions the kernels call): every span of a launch
+//     is taken by exactly one wave, and a span wave's span lies inside the
+//     tensor its chunk record names.
 // Any sanitizer report aborts with a non-zero exit status; the driver prints
 // "OK" at the end.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -259,10 +264,83 @@ static void oracle_calls() {
     }
 }
 
+// Tensor streams of seeded random sizes (tiny runs, multiples of the span
+// and chunk lengths, long tensors), random ranges inside them, shard
+// misalignments 0..7 and chunk shifts 10..13 (a third of them with span
+// starts 7 elements past chunk starts, where the claims change): the hard waves
+// (zp::hard_wave_span) and the span waves (zp::span_claimed on the record of
+// the chunk holding F(w) - 7) take every span exactly once.
+static void reduce_wave_plan() {
+    for (int it = 0; it < 4000; ++it) {
+        const int nt = 1 + int(next_u64() % 400);
+        const int kind = int(next_u64() % 4);
+        std::vector<int64_t> off;
+        int64_t psi = 0;
+        for (int k = 0; k < nt; ++k) {
+            int64_t n;
+            switch ((kind + int(next_u64() % 3)) % 5) {
+                case 0: n = 1 + int64_t(next_u64() % 16); break;
+                case 1: n = 1 + int64_t(next_u64() % 3000); break;
+                case 2: n = 1024 * (1 + int64_t(next_u64() % 4)) - 8 + int64_t(next_u64() % 17); break;
+                case 3: n = 2048 * (1 + int64_t(next_u64() % 3)); break;
+                default: n = 1 + int64_t(next_u64() % 40000); break;
+            }
+            off.push_back(psi);
+            psi += n;
+        }
+        off.push_back(psi);   // sentinel: the end of the last tensor
+        const int shift = 10 + int(next_u64() % 4);
+        const int mis = int(next_u64() % 8);
+        zp::ReduceLaunch a{};
+        a.base = int64_t(next_u64() % uint64_t(psi));
+        a.g_lo = a.base + int64_t(next_u64() % uint64_t(psi - a.base));
+        if (it % 3 == 0) {
+            // the range starts at the shard's start and F(w) - 7 falls on
+            // chunk starts: base - mis - 7 is a multiple of the chunk
+            const int64_t c = int64_t(1) << shift;
+            const int64_t b = (a.base / c) * c + 7 + mis;
+            if (b < psi) a.base = b;
+            a.g_lo = a.base;
+        }
+        a.g_hi = a.g_lo + 1 + int64_t(next_u64() % uint64_t(psi - a.g_lo));
+        a.chunk_shift = shift;
+        zp::plan_reduce_waves(off.data(), int64_t(off.size()), shift, mis, &a);
+        const zp::SpanGeometry geo = zp::span_geometry(a.base, a.g_lo - a.base, a.g_hi - a.base, mis);
+        CHECK(a.n_span == geo.n_span);
+        CHECK(geo.span0 <= a.g_lo && geo.span0 + zp::kOwnerSpanElems * geo.n_span >= a.g_hi);
+        std::vector<int> taken(size_t(geo.n_span), 0);
+        for (int64_t wave = 0; wave < a.n_hard; ++wave) {
+            const int64_t w = zp::hard_wave_span(a, geo, off.data(), wave);
+            if (w < 0) continue;
+            CHECK(w < geo.n_span);
+            if (w < geo.n_span) ++taken[size_t(w)];
+        }
+        for (int64_t w = 1; w + 1 < geo.n_span; ++w) {
+            const int64_t f = geo.span0 + zp::kOwnerSpanElems * w;
+            const int64_t cs = ((f - 7) >> shift) << shift;
+            // the tensor holding the chunk start, as the chunk record names it
+            const size_t t = size_t(std::upper_bound(off.begin(), off.end() - 1, cs) - off.begin()) - 1;
+            const int64_t t_len = off[t + 1] - off[t];
+            if (zp::span_claimed(off[t], t_len, f)) continue;
+            ++taken[size_t(w)];
+            CHECK(f - 7 >= off[t] && f + zp::kOwnerSpanElems + 8 <= off[t] + t_len);
+        }
+        for (int64_t w = 0; w < geo.n_span; ++w) {
+            if (taken[size_t(w)] != 1) {
+                std::fprintf(stderr, "span %lld of %lld taken %d times (iteration %d)\n", (long long)w,
+                             (long long)geo.n_span, taken[size_t(w)], it);
+                g_fail = 1;
+                break;
+            }
+        }
+    }
+}
+
 int main() {
     layouts();
     argument_errors();
     oracle_calls();
+    reduce_wave_plan();
     if (g_fail) return 1;
     std::printf("OK\n");
     return 0;
