@@ -35,6 +35,7 @@ struct zero_layout {
 
     // device tables of the pack (filled by zero_layout_bind_tensors)
     int device = -1;
+    std::vector<int64_t> p_off;   // host copy of the sources' flat offsets, then psi
     zp::PackSrc* d_src = nullptr;
     int32_t* d_first = nullptr;
     int32_t n_src = 0;
@@ -71,6 +72,7 @@ void free_device_tables(zero_layout* l) {
     l->d_first = nullptr;
     l->device = -1;
     l->n_src = 0;
+    l->p_off.clear();
 }
 
 void free_reduce_tables(zero_layout* l) {
@@ -376,6 +378,11 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     }
     if (!chunk_index(offs, l->psi, &shift, &first))
         return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    try {
+        offs.push_back(l->psi);   // the boundaries of the work order end with psi
+    } catch (...) {
+        return zp::fail(ZERO_ERR_OUT_OF_MEMORY, "host table allocation failed");
+    }
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -411,6 +418,7 @@ extern "C" int zero_layout_bind_tensors(zero_layout* l, const uint16_t* const* d
     l->n_src = int32_t(src.size());
     l->chunk_shift = shift;
     l->device = dev;
+    l->p_off.swap(offs);
     return ZERO_OK;
 }
 
@@ -440,6 +448,11 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     a.fill_base = fill * l->bucket;
     a.bucket_elems = l->bucket;
     a.bucket = bucket;
+    a.n_span = (l->bucket + zp::kSpanElems - 1) / zp::kSpanElems;
+    const int64_t data = std::min(l->bucket, l->psi - a.fill_base);   // > 0: fill < n_fills
+    a.n_data_span = (data + zp::kSpanElems - 1) / zp::kSpanElems;
+    a.hard = zp::plan_hard_waves(l->p_off.data(), int64_t(l->p_off.size()), l->chunk_shift, a.fill_base,
+                                 a.n_data_span);
     hipStream_t st = static_cast<hipStream_t>(stream);
     zp::KernelEvents ev;
     e = zp::timing_events(&ev);
@@ -613,22 +626,29 @@ int owner_tables(const zero_layout* l, int32_t rank, ReduceLaunch* out, int* bou
     return ZERO_OK;
 }
 
+HardWaves plan_hard_waves(const int64_t* off, int64_t n_off, int chunk_shift, int64_t span0, int64_t n_span) {
+    HardWaves h;
+    h.n_hard = 2;
+    h.b_first = 0;
+    h.hard_per_b = int32_t((int64_t(1) << chunk_shift) / kSpanElems + 2);
+    if (n_span < 3) return h;   // no interior span
+    // boundaries that can claim an interior span: cs(F(1) - 7) < b < F(n_span - 1) + 8
+    const int64_t lo = ((span0 + kSpanElems - 7) >> chunk_shift) << chunk_shift;
+    const int64_t hi = span0 + kSpanElems * (n_span - 1) + 8;
+    const int64_t* first = std::upper_bound(off, off + n_off, lo);
+    const int64_t* last = std::lower_bound(off, off + n_off, hi);
+    h.b_first = int64_t(first - off);
+    h.n_hard = 2 + (last > first ? int64_t(last - first) : 0) * h.hard_per_b;
+    return h;
+}
+
 void plan_reduce_waves(const int64_t* off, int64_t n_off, int chunk_shift, int mis, ReduceLaunch* a) {
     a->n_span = 0;
-    a->n_hard = 2;
-    a->b_first = 0;
-    a->hard_per_b = int32_t((int64_t(1) << chunk_shift) / kOwnerSpanElems + 2);
+    a->hard = plan_hard_waves(off, n_off, chunk_shift, 0, 0);
     if (a->g_hi <= a->g_lo) return;
     const SpanGeometry g = span_geometry(a->base, a->g_lo - a->base, a->g_hi - a->base, mis);
     a->n_span = g.n_span;
-    if (g.n_span < 3) return;   // no interior span
-    // boundaries that can claim an interior span: cs(F(1) - 7) < b < F(n_span - 1) + 8
-    const int64_t lo = ((g.span0 + kOwnerSpanElems - 7) >> chunk_shift) << chunk_shift;
-    const int64_t hi = g.span0 + kOwnerSpanElems * (g.n_span - 1) + 8;
-    const int64_t* first = std::upper_bound(off, off + n_off, lo);
-    const int64_t* last = std::lower_bound(off, off + n_off, hi);
-    a->b_first = int64_t(first - off);
-    a->n_hard = 2 + (last > first ? int64_t(last - first) : 0) * a->hard_per_b;
+    a->hard = plan_hard_waves(off, n_off, chunk_shift, g.span0, g.n_span);
 }
 
 bool contributions_overlap(const zero_layout* l, uintptr_t lo, uintptr_t hi) {

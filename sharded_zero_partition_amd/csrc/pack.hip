@@ -61,23 +61,48 @@ __device__ __forceinline__ int find_src_in(const PackSrc* __restrict__ src, int 
     return lo;
 }
 
-// Wave w owns bucket elements [w*span, (w+1)*span), span = 512 * U; lane l
-// handles the U vectors at offsets 512 u + 8 l, so each of the U store
-// instructions covers 1 KiB of the bucket contiguously.  The wave reads the
-// source range of its span from the chunk index (two scalar loads); a span
-// inside one tensor takes the cooperative path below, otherwise every lane
+// Cooperative path of a full span inside one tensor: the misalignment phase
+// ph is the same for the whole wave, so each lane loads a single aligned
+// block per vector group from base0 on and takes the block after it from the
+// next lane (the last lane of a group from the next group's first lane, and
+// of the last group from one extra block read by the whole wave).
+template <int U>
+__device__ __forceinline__ void pack_coop(const PackLaunch& a, const uint16_t* base0, int ph, int64_t o_wave,
+                                          int lane) {
+    constexpr int64_t kSpan = 512 * U;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = ld16(base0 + 512 * u + 8 * lane);
+    u32x4 extra = v[U - 1];
+    if (ph) extra = ld16(base0 + kSpan);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u32x4 nxt;
+        nxt.x = __shfl_down(v[u].x, 1);
+        nxt.y = __shfl_down(v[u].y, 1);
+        nxt.z = __shfl_down(v[u].z, 1);
+        nxt.w = __shfl_down(v[u].w, 1);
+        const u32x4 head = u + 1 < U ? v[u + 1 < U ? u + 1 : u] : extra;
+        u32x4 first_of_next;
+        first_of_next.x = __shfl(head.x, 0);
+        first_of_next.y = __shfl(head.y, 0);
+        first_of_next.z = __shfl(head.z, 0);
+        first_of_next.w = __shfl(head.w, 0);
+        if (lane == 63) nxt = first_of_next;
+        const int64_t o = o_wave + 512 * u + 8 * lane;
+        *reinterpret_cast<u32x4*>(a.bucket + o) = window8(v[u], nxt, ph);
+    }
+}
+
+// Any span of the fill, starting at bucket element o_wave: the wave reads the
+// source range of its span from the chunk index (two scalar loads); a full
+// span inside one tensor takes the cooperative path, otherwise every lane
 // finds its own source inside that range and issues the loads of all U
 // vectors before any of them is used (up to 2U 16-byte loads in flight).
 template <int U>
-__global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunch a) {
+__device__ __forceinline__ void pack_general(const PackLaunch& a, int64_t o_wave, int lane) {
     constexpr int64_t kSpan = 512 * U;
-    const int lane = threadIdx.x & 63;
-    // wave-uniform values live in scalar registers; the table reads below
-    // then go through the scalar cache
-    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t wave = int64_t(blockIdx.x) * (kPackThreads / 64) + wave_in_block;
-    const int64_t o_wave = wave * kSpan;
-    if (o_wave >= a.bucket_elems) return;   // the whole wave leaves together
     const int64_t g_wave = a.fill_base + o_wave;
     int lo = 0, hi = 0;
     if (g_wave < a.psi) {
@@ -87,46 +112,19 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
         lo = a.first[g_wave >> a.chunk_shift];
         hi = a.first[(g_last >> a.chunk_shift) + 1];
     }
-    // when the whole span lies in one tensor (the common case) its table
-    // entry is wave-uniform and read once through the scalar cache
+    // when the whole span lies in one tensor its table entry is wave-uniform
+    // and read once through the scalar cache
     const bool one_src = lo == hi;
     PackSrc uni = {nullptr, 0, 0};
     if (one_src && g_wave < a.psi) uni = a.src[lo];
 
-    // Cooperative path: a full span inside one tensor has one misalignment
-    // phase for the whole wave, so each lane loads a single aligned block and
-    // takes the block after it from the next lane (the last lane of a group
-    // from the next group's first lane, and of the last group from one extra
-    // block read by the whole wave).
     if (one_src && o_wave + kSpan <= a.bucket_elems && g_wave + kSpan <= a.psi) {
         const uint16_t* p0 = uni.ptr + (g_wave - uni.flat_off);
         const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
         const uint16_t* base0 = p0 - ph;
         const int64_t need = ph ? kSpan + 8 : kSpan;     // elements read from base0 on
         if (base0 >= uni.ptr && base0 + need <= uni.ptr + uni.len) {
-            u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                v[u] = ld16(base0 + 512 * u + 8 * lane);
-            u32x4 extra = v[U - 1];
-            if (ph) extra = ld16(base0 + kSpan);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                u32x4 nxt;
-                nxt.x = __shfl_down(v[u].x, 1);
-                nxt.y = __shfl_down(v[u].y, 1);
-                nxt.z = __shfl_down(v[u].z, 1);
-                nxt.w = __shfl_down(v[u].w, 1);
-                const u32x4 head = u + 1 < U ? v[u + 1 < U ? u + 1 : u] : extra;
-                u32x4 first_of_next;
-                first_of_next.x = __shfl(head.x, 0);
-                first_of_next.y = __shfl(head.y, 0);
-                first_of_next.z = __shfl(head.z, 0);
-                first_of_next.w = __shfl(head.w, 0);
-                if (lane == 63) nxt = first_of_next;
-                const int64_t o = o_wave + 512 * u + 8 * lane;
-                *reinterpret_cast<u32x4*>(a.bucket + o) = window8(v[u], nxt, ph);
-            }
+            pack_coop<U>(a, base0, ph, o_wave, lane);
             return;
         }
     }
@@ -192,13 +190,64 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
     }
 }
 
+// Wave order as the launch plan sets it (PackLaunch::hard): the first n_hard
+// waves take the two ends of the fill's data and the spans near tensor
+// boundaries; wave n_hard + w takes span w: zeros past the data, else the
+// cooperative path unless a boundary claims the span.  Lane l handles the U
+// vectors at offsets 512 u + 8 l of its span, so each of the U store
+// instructions covers 1 KiB of the bucket contiguously.
+template <int U>
+__global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunch a) {
+    constexpr int64_t kSpan = 512 * U;
+    static_assert(kSpan == kSpanElems, "the work order's span");
+    const int lane = threadIdx.x & 63;
+    // wave-uniform values live in scalar registers; the table reads below
+    // then go through the scalar cache
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wave = int64_t(blockIdx.x) * (kPackThreads / 64) + wave_in_block;
+    if (wave >= a.hard.n_hard) {
+        const int64_t w = wave - a.hard.n_hard;
+        if (w >= a.n_span) return;   // the whole wave leaves together
+        const int64_t o_wave = w * kSpan;
+        if (w >= a.n_data_span) {
+            // past the end of the last tensor: zeros
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = o_wave + 512 * u + 8 * lane;
+                if (o + 8 <= a.bucket_elems) {
+                    *reinterpret_cast<u32x4*>(a.bucket + o) = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    for (int64_t e = o; e < a.bucket_elems; ++e) a.bucket[e] = 0;
+                }
+            }
+            return;
+        }
+        if (w == 0 || w == a.n_data_span - 1) return;   // hard waves 0 and 1
+        const int64_t f = a.fill_base + o_wave;
+        const PackSrc t = a.src[a.first[(f - 7) >> a.chunk_shift]];
+        if (span_claimed(t.flat_off, t.len, f)) return;   // a hard wave's span
+        const uint16_t* p0 = t.ptr + (f - t.flat_off);   // f - 7 >= t.flat_off
+        const int ph = int((reinterpret_cast<uintptr_t>(p0) & 15) >> 1);
+        const uint16_t* base0 = p0 - ph;
+        const int64_t need = ph ? kSpan + 8 : kSpan;
+        if (base0 >= t.ptr && base0 + need <= t.ptr + t.len)
+            pack_coop<U>(a, base0, ph, o_wave, lane);
+        else   // not reached: an unclaimed span lies inside t with 8 elements after it
+            pack_general<U>(a, o_wave, lane);
+        return;
+    }
+    const int64_t w = hard_wave_span(wave, a.n_data_span, a.fill_base, a.hard, a.chunk_shift,
+                                     [&](int64_t i) { return i < a.n_src ? a.src[i].flat_off : a.psi; });
+    if (w < 0) return;
+    pack_general<U>(a, w * kSpan, lane);
+}
+
 constexpr int kPackSpanU = 2;
 
 }  // namespace
 
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEvents& ev) {
-    constexpr int64_t kSpan = 512 * kPackSpanU;
-    const int64_t waves = (a.bucket_elems + kSpan - 1) / kSpan;
+    const int64_t waves = a.hard.n_hard + a.n_span;
     constexpr int64_t kWavesPerBlock = kPackThreads / 64;
     int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks < 1) blocks = 1;

@@ -609,7 +609,7 @@ __device__ __forceinline__ void general_span(const typename Epi::Launch& a, int6
     }
 }
 
-static_assert(kSpanVec == kOwnerSpanVec, "one span geometry for host and device");
+static_assert(kSpanVec == kSpanVecs, "one span geometry for host and device");
 
 // The wave's work, in the order the launch plan sets (ReduceLaunch): the
 // first n_hard waves take the two ends of the range and the spans near
@@ -626,12 +626,12 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     const SpanGeometry geo = span_geometry(a.base, j_lo, j_hi, mis);
     bool bad = false;
 
-    if (wave >= a.n_hard) {
+    if (wave >= a.hard.n_hard) {
         // interior span w: whole and inside the range
-        const int64_t w = wave - a.n_hard;
+        const int64_t w = wave - a.hard.n_hard;
         if (w < 1 || w >= geo.n_span - 1) return;   // the whole wave leaves together
         const int64_t kw = geo.k_lo + w * kSpanVec;
-        const int64_t f = geo.span0 + w * kOwnerSpanElems;
+        const int64_t f = geo.span0 + w * kSpanElems;
         // the epilogue's own loads (p, m, v for the owner step) need only the
         // span's position: issued first, their latency overlaps the record's
         typename Epi::SpanPre pre;
@@ -654,7 +654,7 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
             // with 7 elements before it and 8 after it); kept so that no read
             // can leave a tensor: element by element, each found by search.
 #pragma unroll 1
-            for (int e = 0; e < int(kOwnerSpanElems / 64); ++e) {
+            for (int e = 0; e < int(kSpanElems / 64); ++e) {
                 const int64_t j = kw * 8 - mis + 64 * e + lane;
                 const int64_t g = a.base + j;
                 const int i = search(a.off, 0, a.n_src - 1, g);
@@ -665,7 +665,8 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
         return;
     }
 
-    const int64_t w = hard_wave_span(a, geo, a.off, wave);
+    const int64_t w = hard_wave_span(wave, geo.n_span, geo.span0, a.hard, a.chunk_shift,
+                                     [&](int64_t i) { return a.off[i]; });
     if (w < 0) return;
     general_span<R, Epi>(a, geo.k_lo + w * kSpanVec, geo.k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
     Epi::finish(a, bad);
@@ -707,7 +708,7 @@ __global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsign
 
 // Workgroups of the launch plan: n_hard waves, then one wave per span.
 dim3 plan_grid(const ReduceLaunch& a) {
-    const int64_t waves = a.n_hard + a.n_span;
+    const int64_t waves = a.hard.n_hard + a.n_span;
     int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
     if (blocks < 1) blocks = 1;
     return dim3{unsigned(blocks)};

@@ -26,6 +26,86 @@ struct KernelEvents {
 void clear_error();
 
 // ---------------------------------------------------------------------------
+// work order of the span kernels (pack, reduce-to-owner, owner step)
+// ---------------------------------------------------------------------------
+
+// A wave of these kernels owns a span of kSpanElems consecutive elements
+// (kSpanVecs vectors of 8); span w starts at flat index span0 + kSpanElems w.
+// A span inside one tensor takes a cooperative path (one aligned load per
+// lane and contribution, the misalignment fixed up by cross-lane shuffles);
+// a span near a tensor boundary takes a slower one.  So that the slow spans
+// do not end up among the last waves of a launch, where their longer
+// latency would hold up the launch's end, the first n_hard waves take them:
+//   wave 0 and wave 1: spans 0 and n_span - 1 (the ends of the range);
+//   wave 2 + hard_per_b q + j: the j-th span "claimed" by boundary b_first + q.
+// The boundaries are the flat offsets of the tensors, then psi (the end of
+// the last tensor).  Boundary b claims the interior span w
+// (1 <= w <= n_span - 2) when
+//     cs(F(w) - 7) < b < F(w + 1) + 8,
+// F(w) being the span's first flat index and cs(x) the start of the chunk
+// (of the tables' chunk index) holding x; a span claimed by several
+// boundaries belongs to the lowest.  A boundary claims at most
+// chunk / kSpanElems + 2 spans, the value of hard_per_b.
+// Wave n_hard + w takes the interior span w when no boundary claims it.  It
+// reads the tensor t holding the start of the chunk that holds F(w) - 7: t's
+// end is the first boundary after that chunk start, so no boundary claims
+// the span exactly when t ends at or after F(w + 1) + 8, and then t holds
+// the span, the 7 elements before it and the 8 after it.
+constexpr int64_t kSpanVecs = 128;
+constexpr int64_t kSpanElems = 8 * kSpanVecs;
+constexpr int kSpanShift = 10;
+static_assert(int64_t(1) << kSpanShift == kSpanElems, "span length");
+
+struct HardWaves {
+    int64_t n_hard;      // waves ahead of the span waves
+    int64_t b_first;     // first boundary (index into the offsets) that claims a span
+    int32_t hard_per_b;  // waves per boundary
+};
+
+// The plan for n_span spans from flat index span0, with off the host copy of
+// the boundaries (n_off ascending flat offsets, the last psi) and
+// chunk_shift that of the tables.  Pure host arithmetic.
+HardWaves plan_hard_waves(const int64_t* off, int64_t n_off, int chunk_shift, int64_t span0, int64_t n_span);
+
+// The span hard wave `wave` (< n_hard) takes, or -1.  off(i) is boundary i.
+template <class Off>
+__host__ __device__ inline int64_t hard_wave_span(int64_t wave, int64_t n_span, int64_t span0, const HardWaves& h,
+                                                  int chunk_shift, const Off& off) {
+    if (wave < 2) {   // the ends of the range
+        if (wave == 1 && n_span == 1) return -1;
+        return wave == 0 ? 0 : n_span - 1;
+    }
+    // the j-th span claimed by boundary i, less those the previous boundary
+    // claims (the boundaries claiming one span are consecutive)
+    const int64_t q = (wave - 2) / h.hard_per_b;
+    const int64_t j = (wave - 2) - q * h.hard_per_b;
+    const int64_t i = h.b_first + q;
+    const int s = chunk_shift;
+    const int64_t b = off(i);
+    const int64_t nc = (((b - 1) >> s) + 1) << s;            // cs(x) < b exactly when x < nc
+    int64_t w_lo = (b - 8 - span0) >> kSpanShift;            // F(w + 1) + 8 > b
+    int64_t w_hi = (nc + 6 - span0) >> kSpanShift;           // F(w) - 7 < nc
+    if (i > h.b_first) {
+        const int64_t bp = off(i - 1);
+        const int64_t ncp = (((bp - 1) >> s) + 1) << s;
+        // the previous boundary claims w while F(w) - 7 < ncp
+        const int64_t w_new = (ncp + 7 - span0 + kSpanElems - 1) >> kSpanShift;
+        if (w_new > w_lo) w_lo = w_new;
+    }
+    if (w_lo < 1) w_lo = 1;
+    if (w_hi > n_span - 2) w_hi = n_span - 2;
+    const int64_t w = w_lo + j;
+    return w > w_hi ? -1 : w;
+}
+
+// Whether a boundary claims the interior span starting at flat index f,
+// from the tensor holding the start of the chunk that holds f - 7 (its flat
+// offset and length).
+__host__ __device__ inline bool span_claimed(int64_t t_off, int64_t t_len, int64_t f) {
+    return t_off + t_len < f + kSpanElems + 8;
+}
+
+// ---------------------------------------------------------------------------
 // pack kernel tables
 // ---------------------------------------------------------------------------
 
@@ -46,6 +126,9 @@ struct PackLaunch {
     int64_t fill_base;        // fill * B
     int64_t bucket_elems;     // B
     uint16_t* bucket;         // device, 16-byte aligned
+    int64_t n_span;           // spans of the fill: ceil(B / kSpanElems)
+    int64_t n_data_span;      // spans holding elements below psi (the rest are zeros)
+    HardWaves hard;           // the work order over spans [0, n_data_span)
 };
 
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEvents& ev);
@@ -61,15 +144,10 @@ constexpr int kMaxReduceRanks = 16;
 // bytes padding, then R device addresses (24 + 8 r); rounded up to 16.
 constexpr int chunk_rec_bytes(int R) { return (24 + 8 * R + 15) / 16 * 16; }
 
-// Work of the reduce-to-owner and owner-step kernels.  The owner's shard is
-// cut into 8-element vectors on its own 16-byte grid (vector k covers shard
+// The reduce-to-owner and owner-step kernels cut the owner's shard into
+// 8-element vectors on its own 16-byte grid (vector k covers shard
 // positions [8k - mis, 8k - mis + 8), mis = the shard's misalignment in
-// elements), and a span is kOwnerSpanVec consecutive vectors starting at the
-// vector holding the range's first position.  Span w then starts at flat
-// index span0 + kOwnerSpanElems * w.
-constexpr int64_t kOwnerSpanVec = 128;
-constexpr int64_t kOwnerSpanElems = 8 * kOwnerSpanVec;
-
+// elements); span 0 starts at the vector holding the range's first position.
 struct SpanGeometry {
     int64_t k_lo;     // first vector
     int64_t k_end;    // one past the last vector
@@ -83,29 +161,10 @@ __host__ __device__ inline SpanGeometry span_geometry(int64_t base, int64_t j_lo
     SpanGeometry g;
     g.k_lo = (j_lo + mis) >> 3;
     g.k_end = ((j_hi - 1 + mis) >> 3) + 1;
-    g.n_span = (g.k_end - g.k_lo + kOwnerSpanVec - 1) / kOwnerSpanVec;
+    g.n_span = (g.k_end - g.k_lo + kSpanVecs - 1) / kSpanVecs;
     g.span0 = base + 8 * g.k_lo - mis;
     return g;
 }
-
-// The order of the work.  A span with a tensor boundary near it takes a
-// slower path than one inside a single tensor; so that those spans do not
-// end up in the last waves of a launch, where their longer latency would
-// hold up the launch's end, the first n_hard waves take them:
-//   wave 0 and wave 1: spans 0 and n_span - 1 (the ends of the range);
-//   waves 2 + hard_per_b * q + j: the j-th span "claimed" by boundary
-//     b_first + q, i.e. by the flat index off[b_first + q] (tensor starts,
-//     and psi as a final sentinel entry).
-// Boundary b claims the interior span w (1 <= w <= n_span - 2) when
-//     cs(F(w) - 7) < b < F(w + 1) + 8,
-// F(w) being the span's first flat index and cs(x) the start of the chunk
-// holding x; a span claimed by several boundaries belongs to the lowest.
-// Wave n_hard + w takes span w when no boundary claims it.  It reads the
-// record of the chunk holding F(w) - 7 (the tensor t holding that chunk's
-// start): no boundary claims the span exactly when t ends at or after
-// F(w + 1) + 8, since t's end is the first boundary after the chunk start.
-// Then t holds the span, the 7 elements before it and the 8 after it.  A boundary claims
-// at most (chunk / kOwnerSpanElems) + 2 spans, the value of hard_per_b.
 
 struct ReduceLaunch {
     const int64_t* off;          // device, n_src + 1 flat offsets (sorted; off[n_src] = psi)
@@ -122,59 +181,13 @@ struct ReduceLaunch {
     int64_t base;                // flat index of shard[0] (rank * S)
     uint16_t* shard;             // device, 2-byte aligned
     int64_t n_span;              // spans of the range (span_geometry)
-    int64_t n_hard;              // waves ahead of the span waves (2 + hard_per_b * boundaries)
-    int64_t b_first;
-    int32_t hard_per_b;
+    HardWaves hard;              // the work order (plan_hard_waves over the offsets)
 };
 
-// Fills n_span, n_hard, b_first and hard_per_b of `a` (whose range and base
-// are set) for a shard misaligned by `mis` elements; off is the host copy of
-// the flat offsets (n_off entries, the last psi) and chunk_shift that of the
-// tables.  Pure host arithmetic.
+// Fills n_span and hard of `a` (whose range and base are set) for a shard
+// misaligned by `mis` elements; off, n_off and chunk_shift as for
+// plan_hard_waves.
 void plan_reduce_waves(const int64_t* off, int64_t n_off, int chunk_shift, int mis, ReduceLaunch* a);
-
-constexpr int kOwnerSpanShift = 10;
-static_assert(int64_t(1) << kOwnerSpanShift == kOwnerSpanElems, "span length");
-
-// The span hard wave `wave` (< a.n_hard) takes, or -1.  off is a.off on the
-// device and the same offsets on the host.
-__host__ __device__ inline int64_t hard_wave_span(const ReduceLaunch& a, const SpanGeometry& geo,
-                                                  const int64_t* off, int64_t wave) {
-    if (wave < 2) {   // the ends of the range
-        if (wave == 1 && geo.n_span == 1) return -1;
-        return wave == 0 ? 0 : geo.n_span - 1;
-    }
-    // the j-th span claimed by boundary i: the interior spans w with
-    // cs(F(w) - 7) < b < F(w + 1) + 8, less those the previous boundary
-    // claims (the boundaries claiming one span are consecutive)
-    const int64_t h = wave - 2;
-    const int64_t q = h / a.hard_per_b;
-    const int64_t j = h - q * a.hard_per_b;
-    const int64_t i = a.b_first + q;
-    const int s = a.chunk_shift;
-    const int64_t b = off[i];
-    const int64_t nc = (((b - 1) >> s) + 1) << s;                 // cs(x) < b exactly when x < nc
-    int64_t w_lo = (b - 8 - geo.span0) >> kOwnerSpanShift;        // F(w + 1) + 8 > b
-    int64_t w_hi = (nc + 6 - geo.span0) >> kOwnerSpanShift;       // F(w) - 7 < nc
-    if (i > a.b_first) {
-        const int64_t bp = off[i - 1];
-        const int64_t ncp = (((bp - 1) >> s) + 1) << s;
-        // the previous boundary claims w while F(w) - 7 < ncp
-        const int64_t w_new = (ncp + 7 - geo.span0 + kOwnerSpanElems - 1) >> kOwnerSpanShift;
-        if (w_new > w_lo) w_lo = w_new;
-    }
-    if (w_lo < 1) w_lo = 1;
-    if (w_hi > geo.n_span - 2) w_hi = geo.n_span - 2;
-    const int64_t w = w_lo + j;
-    return w > w_hi ? -1 : w;
-}
-
-// Whether a boundary claims the interior span starting at flat index f, from
-// the tensor holding the start of the chunk that holds f - 7 (its flat
-// offset and length): exactly when that tensor ends before f + span + 8.
-__host__ __device__ inline bool span_claimed(int64_t t_off, int64_t t_len, int64_t f) {
-    return t_off + t_len < f + kOwnerSpanElems + 8;
-}
 
 hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev);
 

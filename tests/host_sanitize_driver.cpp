@@ -12,10 +12,10 @@
 //   - argument errors of every entry point that can be called without a
 //     device, with fake (never dereferenced) device addresses;
 //   - the oracle's conversions, reduce, flag and Adam on random data;
-//   - the work order of the reduce-to-owner and owner-step launches (the
-//     same host/device functions the kernels call): every span of a launch
-//     is taken by exactly one wave, and a span wave's span lies inside the
-//     tensor its chunk record names.
+//   - the work order of the pack, reduce-to-owner and owner-step launches
+//     (the same host/device functions the kernels call): every span of a
+//     launch is taken by exactly one wave, and a span wave's span lies
+//     inside the tensor its chunk record names.
 // Any sanitizer report aborts with a non-zero exit status; the driver prints
 // "OK" at the end.
 #include <cmath>
@@ -265,13 +265,16 @@ static void oracle_calls() {
 }
 
 // Tensor streams of seeded random sizes (tiny runs, multiples of the span
-// and chunk lengths, long tensors), random ranges inside them, shard
-// misalignments 0..7 and chunk shifts 10..13 (a third of them with span
-// starts 7 elements past chunk starts, where the claims change): the hard waves
-// (zp::hard_wave_span) and the span waves (zp::span_claimed on the record of
-// the chunk holding F(w) - 7) take every span exactly once.
-static void reduce_wave_plan() {
-    for (int it = 0; it < 4000; ++it) {
+// and chunk lengths, long tensors), random ranges inside them and chunk
+// shifts 10..13; the reduce geometry with shard misalignments 0..7 (a third
+// of the cases with span starts 7 elements past chunk starts, where the
+// claims change) and the pack geometry (spans from the fill's start): the
+// hard waves (zp::hard_wave_span) and the span waves (zp::span_claimed on
+// the tensor holding the start of the chunk that holds F(w) - 7) take every
+// span exactly once, and a span wave's span lies in that tensor with 7
+// elements before it and 8 after it.
+static void span_work_order() {
+    for (int it = 0; it < 6000; ++it) {
         const int nt = 1 + int(next_u64() % 400);
         const int kind = int(next_u64() % 4);
         std::vector<int64_t> off;
@@ -288,47 +291,63 @@ static void reduce_wave_plan() {
             off.push_back(psi);
             psi += n;
         }
-        off.push_back(psi);   // sentinel: the end of the last tensor
+        off.push_back(psi);   // the last boundary: the end of the last tensor
         const int shift = 10 + int(next_u64() % 4);
-        const int mis = int(next_u64() % 8);
-        zp::ReduceLaunch a{};
-        a.base = int64_t(next_u64() % uint64_t(psi));
-        a.g_lo = a.base + int64_t(next_u64() % uint64_t(psi - a.base));
-        if (it % 3 == 0) {
-            // the range starts at the shard's start and F(w) - 7 falls on
-            // chunk starts: base - mis - 7 is a multiple of the chunk
-            const int64_t c = int64_t(1) << shift;
-            const int64_t b = (a.base / c) * c + 7 + mis;
-            if (b < psi) a.base = b;
-            a.g_lo = a.base;
+        int64_t n_span = 0, span0 = 0;
+        zp::HardWaves h{};
+        if (it % 2 == 0) {
+            // reduce-to-owner / owner step: a range of a shard
+            const int mis = int(next_u64() % 8);
+            zp::ReduceLaunch a{};
+            a.base = int64_t(next_u64() % uint64_t(psi));
+            a.g_lo = a.base + int64_t(next_u64() % uint64_t(psi - a.base));
+            if (it % 3 == 0) {
+                // the range starts at the shard's start and F(w) - 7 falls
+                // on chunk starts: base - mis - 7 is a multiple of the chunk
+                const int64_t c = int64_t(1) << shift;
+                const int64_t b = (a.base / c) * c + 7 + mis;
+                if (b < psi) a.base = b;
+                a.g_lo = a.base;
+            }
+            a.g_hi = a.g_lo + 1 + int64_t(next_u64() % uint64_t(psi - a.g_lo));
+            zp::plan_reduce_waves(off.data(), int64_t(off.size()), shift, mis, &a);
+            const zp::SpanGeometry geo = zp::span_geometry(a.base, a.g_lo - a.base, a.g_hi - a.base, mis);
+            CHECK(a.n_span == geo.n_span);
+            CHECK(geo.span0 <= a.g_lo && geo.span0 + zp::kSpanElems * geo.n_span >= a.g_hi);
+            n_span = geo.n_span;
+            span0 = geo.span0;
+            h = a.hard;
+        } else {
+            // pack: the data part of one fill of a bucket
+            const int64_t bucket = 1 + int64_t(next_u64() % uint64_t(psi));
+            const int64_t fill = int64_t(next_u64() % uint64_t((psi + bucket - 1) / bucket));
+            span0 = fill * bucket;
+            const int64_t data = std::min(bucket, psi - span0);
+            n_span = (data + zp::kSpanElems - 1) / zp::kSpanElems;
+            h = zp::plan_hard_waves(off.data(), int64_t(off.size()), shift, span0, n_span);
         }
-        a.g_hi = a.g_lo + 1 + int64_t(next_u64() % uint64_t(psi - a.g_lo));
-        a.chunk_shift = shift;
-        zp::plan_reduce_waves(off.data(), int64_t(off.size()), shift, mis, &a);
-        const zp::SpanGeometry geo = zp::span_geometry(a.base, a.g_lo - a.base, a.g_hi - a.base, mis);
-        CHECK(a.n_span == geo.n_span);
-        CHECK(geo.span0 <= a.g_lo && geo.span0 + zp::kOwnerSpanElems * geo.n_span >= a.g_hi);
-        std::vector<int> taken(size_t(geo.n_span), 0);
-        for (int64_t wave = 0; wave < a.n_hard; ++wave) {
-            const int64_t w = zp::hard_wave_span(a, geo, off.data(), wave);
+        std::vector<int> taken(size_t(n_span), 0);
+        for (int64_t wave = 0; wave < h.n_hard; ++wave) {
+            const int64_t w = zp::hard_wave_span(wave, n_span, span0, h, shift,
+                                                 [&](int64_t i) { return off[size_t(i)]; });
             if (w < 0) continue;
-            CHECK(w < geo.n_span);
-            if (w < geo.n_span) ++taken[size_t(w)];
+            CHECK(w < n_span);
+            if (w < n_span) ++taken[size_t(w)];
         }
-        for (int64_t w = 1; w + 1 < geo.n_span; ++w) {
-            const int64_t f = geo.span0 + zp::kOwnerSpanElems * w;
+        for (int64_t w = 1; w + 1 < n_span; ++w) {
+            const int64_t f = span0 + zp::kSpanElems * w;
             const int64_t cs = ((f - 7) >> shift) << shift;
-            // the tensor holding the chunk start, as the chunk record names it
+            // the tensor holding the chunk start, as the tables name it
             const size_t t = size_t(std::upper_bound(off.begin(), off.end() - 1, cs) - off.begin()) - 1;
             const int64_t t_len = off[t + 1] - off[t];
             if (zp::span_claimed(off[t], t_len, f)) continue;
             ++taken[size_t(w)];
-            CHECK(f - 7 >= off[t] && f + zp::kOwnerSpanElems + 8 <= off[t] + t_len);
+            CHECK(f - 7 >= off[t] && f + zp::kSpanElems + 8 <= off[t] + t_len);
         }
-        for (int64_t w = 0; w < geo.n_span; ++w) {
+        for (int64_t w = 0; w < n_span; ++w) {
             if (taken[size_t(w)] != 1) {
                 std::fprintf(stderr, "span %lld of %lld taken %d times (iteration %d)\n", (long long)w,
-                             (long long)geo.n_span, taken[size_t(w)], it);
+                             (long long)n_span, taken[size_t(w)], it);
                 g_fail = 1;
                 break;
             }
@@ -340,7 +359,7 @@ int main() {
     layouts();
     argument_errors();
     oracle_calls();
-    reduce_wave_plan();
+    span_work_order();
     if (g_fail) return 1;
     std::printf("OK\n");
     return 0;
