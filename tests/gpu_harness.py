@@ -22,6 +22,38 @@ from parity import adam_operand_scales, assert_fp16_close, assert_scaled_close
 
 SENTINEL = 0x5A5A
 
+# The span kernels (pack, reduce-to-owner, owner step) give each wave a span
+# of 1024 consecutive elements, span w starting at flat index F(w) = s0 +
+# 1024 w, and decide which wave takes a span from where tensor boundaries
+# fall: boundary b belongs to span w's decision when cs(F(w) - 7) < b <
+# F(w + 1) + 8, cs being the start of the 2048-element chunk holding its
+# argument.  Boundaries at these offsets from a span start and from a chunk
+# start sit on either side of those inequalities.
+SPAN_MARGINS = (-9, -8, -7, -6, -1, 0, 1, 6, 7, 8, 9)
+CHUNK_MARGINS = (-1, 0, 1, 6, 7, 8)
+
+
+def margin_numels(rng, span0s, psi, span=1024, chunk=2048):
+    """Tensor sizes (summing to psi) whose starts fall at F(w) + d for the
+    span grids that start at each flat index in span0s (d from SPAN_MARGINS,
+    about every other span), at chunk starts + d (CHUNK_MARGINS), and in a
+    few runs of 1..4-element tensors."""
+    starts = set()
+    for s0 in span0s:
+        for f in range(s0 + span, psi, span):
+            if rng.random() < 0.5:
+                starts.add(f + int(rng.choice(SPAN_MARGINS)))
+    for c in range(chunk, psi, chunk):
+        if rng.random() < 0.3:
+            starts.add(c + int(rng.choice(CHUNK_MARGINS)))
+    for _ in range(4):
+        p = int(rng.integers(1, psi - 200))
+        for _ in range(int(rng.integers(2, 30))):
+            p += int(rng.integers(1, 5))
+            starts.add(p)
+    bounds = [0] + sorted(x for x in starts if 0 < x < psi) + [psi]
+    return [b - a for a, b in zip(bounds, bounds[1:])]
+
 
 def device_state(p0: torch.Tensor, pingpong: bool) -> "zp.ShardState":
     p = p0.to("cuda", torch.float32).contiguous().clone()

@@ -24,7 +24,7 @@ import oracle
 import sharded_zero_partition_amd as zp
 from oracle import layout as OL
 from sharded_zero_partition_amd import workloads as W
-from gpu_harness import SENTINEL
+from gpu_harness import SENTINEL, margin_numels
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,31 @@ def _host(lists):
 def _real(olay, rank):
     lo = rank * olay.shard
     return max(0, min(lo + olay.shard, olay.psi) - lo)
+
+
+@pytest.mark.parametrize("R", [1, 2, 7])
+def test_boundaries_at_work_order_margins(R):
+    """Tensor boundaries just before, at and after the offsets where the
+    launch's work order decides which wave takes a span (span starts - 7 and
+    + 8, chunk starts), for both owners of a two-rank layout whose second
+    shard starts 7 elements past a chunk start; two steps each."""
+    rng = np.random.default_rng(800 + R)
+    S = 2048 * 30 + 7
+    psi = 2 * S
+    numels = margin_numels(rng, [0, S], psi)
+    lay = zp.partition_layout(numels, 2, stage=2, align=1, bucket=1 << 16)
+    olay = OL.partition_layout(numels, 2, 2, 1, 1 << 16)
+    assert olay.shard == S
+    bufs, lists = _lists(rng, numels, R)
+    lay.bind_contributions(lists)
+    print(f"[margins] R={R} tensors={len(numels)}", flush=True)
+    runs = [OwnerRun(olay, r, rng, slot_offset=int(rng.integers(0, 8))) for r in range(2)]
+    for step in range(2):
+        host = _host(lists)
+        for r, run in enumerate(runs):
+            assert run.step(lay, r, host) == 0
+        _redraw(rng, bufs)
+    lay.close()
 
 
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 9, 16])

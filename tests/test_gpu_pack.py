@@ -10,6 +10,7 @@ import torch
 import oracle
 import sharded_zero_partition_amd as zp
 from sharded_zero_partition_amd import workloads as W
+from gpu_harness import margin_numels
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +73,23 @@ def test_special_bit_patterns_survive():
     _check_all_fills(tensors, numels, 16)
     tensors, _ = _views_at_offsets(rng, [37, 2, 64])
     _check_all_fills(tensors, [37, 2, 64], 24)
+
+
+@pytest.mark.parametrize("misalign", [False, True])
+def test_boundaries_at_work_order_margins(misalign):
+    """Tensor boundaries just before, at and after the offsets where the
+    launch's work order decides which wave takes a span (span starts - 7 and
+    + 8, chunk starts) in every fill of a bucket of 2048 * 10 + 7 elements
+    (so that F(w) - 7 of the second fill falls on chunk starts), the last
+    fill ending early; tensors aligned or at every alignment phase."""
+    rng = np.random.default_rng(40 + misalign)
+    bucket = 2048 * 10 + 7
+    psi = 4 * bucket + 3001
+    numels = margin_numels(rng, [k * bucket for k in range(5)], psi)
+    tensors, _ = _views_at_offsets(rng, numels, misalign=misalign)
+    print(f"[margins] misalign={misalign} tensors={len(numels)}", flush=True)
+    info = _check_all_fills(tensors, numels, bucket)
+    assert info.n_fills == 5
 
 
 def test_errors():

@@ -13,6 +13,7 @@ import oracle
 import sharded_zero_partition_amd as zp
 from oracle import layout as OL
 from sharded_zero_partition_amd import workloads as W
+from gpu_harness import margin_numels
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +107,45 @@ def test_runs_of_tiny_tensors(R):
             if not np.array_equal(got, want):
                 bad = np.flatnonzero(got != want)
                 raise AssertionError(f"trial {trial} rank {r}: {bad.size} differ, first {bad[0]}")
+            h = holder.cpu().numpy().view(np.uint16)
+            assert (h[:mis] == SENT).all() and (h[mis + S:] == SENT).all()
+        lay.close()
+
+
+@pytest.mark.parametrize("R", [1, 2, 5])
+@pytest.mark.parametrize("mis", [0, 3, 7])
+def test_boundaries_at_work_order_margins(R, mis):
+    """Tensor boundaries just before, at and after the offsets where the
+    launch's work order decides which wave takes a span (span starts - 7 and
+    + 8, chunk starts), for both owners of a two-rank layout whose second
+    shard starts 7 + mis elements past a chunk start (so that F(w) - 7 falls
+    on chunk starts), with the shard base misaligned by mis elements; one fill
+    covering everything and 5000-element fills; against the oracle."""
+    rng = np.random.default_rng(700 + 10 * R + mis)
+    S = 2048 * 30 + 7 + mis
+    psi = 2 * S
+    numels = margin_numels(rng, [-mis, S - mis], psi)
+    lists = _lists(rng, numels, R)
+    host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+    for bucket in (psi, 5000):
+        lay = zp.partition_layout(numels, 2, stage=2, align=1, bucket=bucket)
+        olay = OL.partition_layout(numels, 2, 2, 1, bucket)
+        assert olay.shard == S
+        lay.bind_contributions(lists)
+        print(f"[margins] R={R} mis={mis} tensors={len(numels)} bucket={bucket}", flush=True)
+        for r in range(2):
+            holder = torch.full((S + 16,), SENT, dtype=torch.int16, device="cuda")
+            shard = holder[mis:mis + S]
+            want = np.full(S, SENT, np.uint16)
+            for k in range(olay.n_fills):
+                n = lay.reduce_to_owner(k, r, shard)
+                off, vals = oracle.reduce_to_owner(host, olay, k, r)
+                assert n == vals.size
+                want[off:off + vals.size] = vals
+            got = shard.cpu().numpy().view(np.uint16)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                raise AssertionError(f"bucket {bucket} rank {r}: {bad.size} differ, first {bad[0]}")
             h = holder.cpu().numpy().view(np.uint16)
             assert (h[:mis] == SENT).all() and (h[mis + S:] == SENT).all()
         lay.close()
