@@ -207,7 +207,7 @@ int zero_layout_bind_tensors(zero_layout* layout, const uint16_t* const* dev_ptr
  *   packed_elems  optional host output: min(B, psi - fill * B)
  * Asynchronous on `stream`; must run on the device the layout was bound on.
  * Errors: STATE (not bound, or another device), INVALID_ARG (fill outside
- * [0, n_fills)), ALIGNMENT, HIP. */
+ * [0, n_fills), or B above ZERO_MAX_SHARD_ELEMS), ALIGNMENT, HIP. */
 int zero_pack_bucket(const zero_layout* layout, int64_t fill, uint16_t* bucket,
                      void* stream, int64_t* packed_elems);
 
@@ -243,7 +243,8 @@ int zero_layout_bind_contributions(zero_layout* layout, int32_t R,
  *            rank's shard do not meet)
  * Asynchronous on `stream`; must run on the device the contributions were
  * bound on.  Errors: STATE (no bucket plan, not bound, another device),
- * INVALID_ARG (fill or rank out of range), ALIGNMENT, HIP. */
+ * INVALID_ARG (fill or rank out of range, B above ZERO_MAX_SHARD_ELEMS),
+ * ALIGNMENT, HIP. */
 int zero_reduce_to_owner(const zero_layout* layout, int64_t fill, int32_t rank,
                          uint16_t* shard, void* stream, int64_t* written);
 
@@ -291,10 +292,12 @@ typedef struct zero_adam_hparams {
  * fp32 range: a clean step never turns a finite gradient into inf or NaN. */
 #define ZERO_MIN_LOSS_SCALE 5.9604644775390625e-08f
 
-/* Largest shard a step call takes (4096 * (2^31 - 1) elements, about 8.8e12):
- * a pass is one launch of at most 2^31 - 1 workgroups of 4096 elements.
- * Larger shard_elems fail with ZERO_ERR_INVALID_ARG. */
-#define ZERO_MAX_SHARD_ELEMS 8796093018112LL
+/* Largest shard a step call takes, and largest bucket the pack and the
+ * reduce-to-owner take (4096 * (2^24 - 1) elements, about 6.9e10): a pass is
+ * one launch of 256-thread workgroups of 4096 elements each, and HIP takes
+ * fewer than 2^32 work-items per grid dimension, so at most 2^24 - 1 of them.
+ * Larger shard_elems (or bucket_elems) fail with ZERO_ERR_INVALID_ARG. */
+#define ZERO_MAX_SHARD_ELEMS 68719472640LL
 typedef struct zero_loss_scaler {
     float scale;           /* the contributions were multiplied by this */
     float backoff;

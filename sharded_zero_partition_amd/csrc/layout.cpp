@@ -427,6 +427,8 @@ extern "C" int zero_pack_bucket(const zero_layout* l, int64_t fill, uint16_t* bu
     zp::clear_error();
     if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
     if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (l->bucket > ZERO_MAX_SHARD_ELEMS)
+        return zp::fail(ZERO_ERR_INVALID_ARG, "bucket_elems above ZERO_MAX_SHARD_ELEMS (one launch's grid)");
     if (l->device < 0) return zp::fail(ZERO_ERR_STATE, "tensors not bound (zero_layout_bind_tensors)");
     if (fill < 0 || fill >= l->n_fills) return zp::fail(ZERO_ERR_INVALID_ARG, "fill out of range");
     if (!bucket) return zp::fail(ZERO_ERR_INVALID_ARG, "bucket is NULL");
@@ -637,8 +639,16 @@ HardWaves plan_hard_waves(const int64_t* off, int64_t n_off, int chunk_shift, in
     const int64_t hi = span0 + kSpanElems * (n_span - 1) + 8;
     const int64_t* first = std::upper_bound(off, off + n_off, lo);
     const int64_t* last = std::lower_bound(off, off + n_off, hi);
+    const int64_t n_b = last > first ? int64_t(last - first) : 0;
+    if (n_b * h.hard_per_b > 8 * n_span + 1024 || 2 + n_b * h.hard_per_b + n_span > kMaxGridWaves) {
+        // boundary waves far outnumbering the spans, or a grid past the
+        // launch limit: the launch runs in order
+        h.n_hard = 0;
+        h.hard_per_b = 0;
+        return h;
+    }
     h.b_first = int64_t(first - off);
-    h.n_hard = 2 + (last > first ? int64_t(last - first) : 0) * h.hard_per_b;
+    h.n_hard = 2 + n_b * h.hard_per_b;
     return h;
 }
 
@@ -665,6 +675,8 @@ extern "C" int zero_reduce_to_owner(const zero_layout* l, int64_t fill, int32_t 
     zp::clear_error();
     if (!l) return zp::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
     if (l->bucket <= 0) return zp::fail(ZERO_ERR_STATE, "layout has no bucket plan");
+    if (l->bucket > ZERO_MAX_SHARD_ELEMS)
+        return zp::fail(ZERO_ERR_INVALID_ARG, "bucket_elems above ZERO_MAX_SHARD_ELEMS (one launch's grid)");
     if (l->r_device < 0)
         return zp::fail(ZERO_ERR_STATE, "contributions not bound (zero_layout_bind_contributions)");
     if (fill < 0 || fill >= l->n_fills) return zp::fail(ZERO_ERR_INVALID_ARG, "fill out of range");

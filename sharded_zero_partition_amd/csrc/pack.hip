@@ -205,6 +205,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
     // then go through the scalar cache
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wave = int64_t(blockIdx.x) * (kPackThreads / 64) + wave_in_block;
+    if (a.hard.hard_per_b == 0) {
+        // in order: wave w takes span w
+        if (wave < a.n_span) pack_general<U>(a, wave * kSpan, lane);
+        return;
+    }
     if (wave >= a.hard.n_hard) {
         const int64_t w = wave - a.hard.n_hard;
         if (w >= a.n_span) return;   // the whole wave leaves together
@@ -248,6 +253,7 @@ constexpr int kPackSpanU = 2;
 
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     const int64_t waves = a.hard.n_hard + a.n_span;
+    if (waves > kMaxGridWaves) return hipErrorInvalidConfiguration;
     constexpr int64_t kWavesPerBlock = kPackThreads / 64;
     int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (blocks < 1) blocks = 1;

@@ -626,6 +626,13 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     const SpanGeometry geo = span_geometry(a.base, j_lo, j_hi, mis);
     bool bad = false;
 
+    if (a.hard.hard_per_b == 0) {
+        // in order: wave w takes span w
+        if (wave >= geo.n_span) return;
+        general_span<R, Epi>(a, geo.k_lo + wave * kSpanVec, geo.k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
+        Epi::finish(a, bad);
+        return;
+    }
     if (wave >= a.hard.n_hard) {
         // interior span w: whole and inside the range
         const int64_t w = wave - a.hard.n_hard;
@@ -708,7 +715,7 @@ __global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsign
 
 // Workgroups of the launch plan: n_hard waves, then one wave per span.
 dim3 plan_grid(const ReduceLaunch& a) {
-    const int64_t waves = a.hard.n_hard + a.n_span;
+    const int64_t waves = a.hard.n_hard + a.n_span;   // <= kMaxGridWaves (checked by the launchers)
     int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
     if (blocks < 1) blocks = 1;
     return dim3{unsigned(blocks)};
@@ -717,6 +724,7 @@ dim3 plan_grid(const ReduceLaunch& a) {
 }  // namespace
 
 hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev) {
+    if (a.hard.n_hard + a.n_span > kMaxGridWaves) return hipErrorInvalidConfiguration;
     const dim3 grid = plan_grid(a);
     switch (a.R) {
         case 1: hipExtLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
@@ -767,6 +775,7 @@ void launch_owner_real(const OwnerLaunch& a, hipStream_t stream, const KernelEve
 }  // namespace
 
 hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
+    if (a.hard.n_hard + a.n_span > kMaxGridWaves) return hipErrorInvalidConfiguration;
     // the shard is [0, a.st.n): its real elements first, then its padding
     const int64_t n_real = a.g_hi - a.g_lo;
     const bool pad = a.st.n > n_real;

@@ -51,15 +51,23 @@ void clear_error();
 // end is the first boundary after that chunk start, so no boundary claims
 // the span exactly when t ends at or after F(w + 1) + 8, and then t holds
 // the span, the 7 elements before it and the 8 after it.
+// When the boundary waves would far outnumber the spans (many tiny tensors
+// in a short range), or the grid would pass the launch limit, the launch
+// runs in order instead (hard_per_b = 0, n_hard = 0): wave w takes span w,
+// whatever it holds.
 constexpr int64_t kSpanVecs = 128;
 constexpr int64_t kSpanElems = 8 * kSpanVecs;
 constexpr int kSpanShift = 10;
 static_assert(int64_t(1) << kSpanShift == kSpanElems, "span length");
 
+// Waves of one launch of 256-thread workgroups: HIP takes fewer than 2^32
+// work-items per grid dimension.
+constexpr int64_t kMaxGridWaves = ((int64_t(1) << 24) - 1) * 4;
+
 struct HardWaves {
     int64_t n_hard;      // waves ahead of the span waves
     int64_t b_first;     // first boundary (index into the offsets) that claims a span
-    int32_t hard_per_b;  // waves per boundary
+    int32_t hard_per_b;  // waves per boundary; 0: in order (no hard waves)
 };
 
 // The plan for n_span spans from flat index span0, with off the host copy of

@@ -272,8 +272,10 @@ static void oracle_calls() {
 // hard waves (zp::hard_wave_span) and the span waves (zp::span_claimed on
 // the tensor holding the start of the chunk that holds F(w) - 7) take every
 // span exactly once, and a span wave's span lies in that tensor with 7
-// elements before it and 8 after it.
+// elements before it and 8 after it.  Launches whose boundary waves would
+// outnumber their spans run in order instead.
 static void span_work_order() {
+    int in_order = 0;
     for (int it = 0; it < 6000; ++it) {
         const int nt = 1 + int(next_u64() % 400);
         const int kind = int(next_u64() % 4);
@@ -327,6 +329,13 @@ static void span_work_order() {
             h = zp::plan_hard_waves(off.data(), int64_t(off.size()), shift, span0, n_span);
         }
         std::vector<int> taken(size_t(n_span), 0);
+        if (h.hard_per_b == 0) {
+            // in order: each wave its own span, only when boundary waves
+            // would outnumber the spans
+            ++in_order;
+            CHECK(h.n_hard == 0 && n_span >= 3);
+            continue;
+        }
         for (int64_t wave = 0; wave < h.n_hard; ++wave) {
             const int64_t w = zp::hard_wave_span(wave, n_span, span0, h, shift,
                                                  [&](int64_t i) { return off[size_t(i)]; });
@@ -352,6 +361,29 @@ static void span_work_order() {
                 break;
             }
         }
+    }
+    // both plans occur: in order in a minority of the cases
+    CHECK(in_order < 60);   // rare in these streams
+    // Dense boundaries: 5000 one-element tensors over 5 spans give about 4100
+    // boundaries that could claim a span, 3 waves each: in order.  The same
+    // stream over 300 spans keeps the work order.
+    {
+        std::vector<int64_t> off;
+        for (int64_t k = 0; k <= 5000; ++k) off.push_back(k);
+        off.push_back(5000 + 300 * 1024);
+        zp::HardWaves h = zp::plan_hard_waves(off.data(), int64_t(off.size()), 10, 0, 5);
+        CHECK(h.hard_per_b == 0 && h.n_hard == 0);
+        h = zp::plan_hard_waves(off.data(), int64_t(off.size()), 10, 0, 2000);
+        CHECK(h.hard_per_b == 3 && h.n_hard > 2);
+    }
+    // a grid past the launch limit runs in order
+    {
+        std::vector<int64_t> off;
+        for (int64_t k = 0; k <= 100; ++k) off.push_back(k * (int64_t(1) << 20));
+        zp::HardWaves h = zp::plan_hard_waves(off.data(), int64_t(off.size()), 30, 0, 100 << 10);
+        CHECK(h.hard_per_b == 0);
+        h = zp::plan_hard_waves(off.data(), int64_t(off.size()), 12, 0, 100 << 10);
+        CHECK(h.hard_per_b == 6);
     }
 }
 

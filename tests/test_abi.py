@@ -176,7 +176,7 @@ def test_shard_step_argument_errors_need_no_device(zp):
     assert call(sc=zp.LossScaler.make(1024.0, min_scale=2.0 ** -25)) == -1
     assert b"2^-24" in zp.lib.zero_last_error()
     st_big = zp.ShardStateC.from_buffer_copy(st)
-    st_big.shard_elems = 4096 * (2 ** 31 - 1) + 1                   # above ZERO_MAX_SHARD_ELEMS
+    st_big.shard_elems = 4096 * (2 ** 24 - 1) + 1                   # above ZERO_MAX_SHARD_ELEMS
     assert call(st=st_big) == -1 and b"ZERO_MAX_SHARD_ELEMS" in zp.lib.zero_last_error()
     # the no-allocation variant takes the same checks before any HIP call
     noalloc = lambda st=st, sc=sc: zp.lib.zero_shard_step_noalloc(  # noqa: E731
@@ -258,6 +258,15 @@ def test_reduce_to_owner_argument_errors_need_no_device(zp):
     n = ctypes.c_int64()
     assert zp.lib.zero_reduce_to_owner(lay._h, 0, 0, ctypes.c_void_p(1 << 32), None,
                                        ctypes.byref(n)) == -7                     # not bound
+    # a fill is one launch: buckets above ZERO_MAX_SHARD_ELEMS are refused
+    big = zp.partition_layout([10, 20], 2, bucket=4096 * (2 ** 24 - 1) + 1)
+    assert zp.lib.zero_reduce_to_owner(big._h, 0, 0, ctypes.c_void_p(1 << 32), None,
+                                       ctypes.byref(n)) == -1
+    assert b"ZERO_MAX_SHARD_ELEMS" in zp.lib.zero_last_error()
+    assert zp.lib.zero_pack_bucket(big._h, 0, ctypes.c_void_p(1 << 32), None, ctypes.byref(n)) == -1
+    assert b"ZERO_MAX_SHARD_ELEMS" in zp.lib.zero_last_error()
+    ok = zp.partition_layout([10, 20], 2, bucket=4096 * (2 ** 24 - 1))
+    assert zp.lib.zero_pack_bucket(ok._h, 0, ctypes.c_void_p(1 << 32), None, ctypes.byref(n)) == -7
 
 
 def test_owner_step_argument_errors_need_no_device(zp):

@@ -144,6 +144,27 @@ def test_boundaries_at_work_order_margins(R):
     lay.close()
 
 
+@pytest.mark.parametrize("R", [1, 2, 7])
+def test_dense_boundaries_run_in_order(R):
+    """Thousands of 1..3-element tensors around one longer tensor: the
+    boundary waves would far outnumber the owner's spans, so the launch runs
+    in order; both owners, two steps each."""
+    rng = np.random.default_rng(950 + R)
+    numels = ([int(x) for x in rng.integers(1, 4, size=3000)] + [5000]
+              + [int(x) for x in rng.integers(1, 4, size=3000)])
+    lay = zp.partition_layout(numels, 2, stage=2, align=8, bucket=8192)
+    olay = OL.partition_layout(numels, 2, 2, 8, 8192)
+    bufs, lists = _lists(rng, numels, R)
+    lay.bind_contributions(lists)
+    runs = [OwnerRun(olay, r, rng, slot_offset=int(rng.integers(0, 8))) for r in range(2)]
+    for step in range(2):
+        host = _host(lists)
+        for r, run in enumerate(runs):
+            assert run.step(lay, r, host) == 0
+        _redraw(rng, bufs)
+    lay.close()
+
+
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 9, 16])
 def test_small_ragged_layouts_every_rank(R):
     rng = np.random.default_rng(500 + R)

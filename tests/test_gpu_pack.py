@@ -92,6 +92,18 @@ def test_boundaries_at_work_order_margins(misalign):
     assert info.n_fills == 5
 
 
+def test_dense_boundaries_run_in_order():
+    """Thousands of 1..3-element tensors around one longer tensor, 8192- and
+    3001-element fills: the boundary waves would far outnumber the spans, so
+    each launch runs in order; every fill against the oracle."""
+    rng = np.random.default_rng(41)
+    numels = ([int(x) for x in rng.integers(1, 4, size=3000)] + [5000]
+              + [int(x) for x in rng.integers(1, 4, size=3000)])
+    tensors, _ = _views_at_offsets(rng, numels)
+    for bucket in (8192, 3001):
+        _check_all_fills(tensors, numels, bucket)
+
+
 def test_errors():
     lay = zp.partition_layout([10, 20], 2, bucket=0)
     with pytest.raises(zp.ZeroError, match="STATE"):

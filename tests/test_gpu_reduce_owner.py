@@ -151,6 +151,40 @@ def test_boundaries_at_work_order_margins(R, mis):
         lay.close()
 
 
+@pytest.mark.parametrize("R", [1, 2, 5])
+def test_dense_boundaries_run_in_order(R):
+    """Thousands of 1..3-element tensors around one longer tensor: the
+    boundary waves would far outnumber the spans of each launch, so the
+    launch runs in order (each wave its own span); every fill and owner of
+    8192-element fills and of one fill, against the oracle."""
+    rng = np.random.default_rng(900 + R)
+    numels = ([int(x) for x in rng.integers(1, 4, size=3000)] + [5000]
+              + [int(x) for x in rng.integers(1, 4, size=3000)])
+    lists = _lists(rng, numels, R)
+    host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+    psi = sum(numels)
+    for bucket in (8192, psi):
+        lay = zp.partition_layout(numels, 2, stage=2, align=8, bucket=bucket)
+        olay = OL.partition_layout(numels, 2, 2, 8, bucket)
+        lay.bind_contributions(lists)
+        S = olay.shard
+        for r in range(2):
+            mis = int(rng.integers(0, 8))
+            holder = torch.full((S + 16,), SENT, dtype=torch.int16, device="cuda")
+            shard = holder[mis:mis + S]
+            want = np.full(S, SENT, np.uint16)
+            for k in range(olay.n_fills):
+                n = lay.reduce_to_owner(k, r, shard)
+                off, vals = oracle.reduce_to_owner(host, olay, k, r)
+                assert n == vals.size
+                want[off:off + vals.size] = vals
+            got = shard.cpu().numpy().view(np.uint16)
+            if not np.array_equal(got, want):
+                bad = np.flatnonzero(got != want)
+                raise AssertionError(f"bucket {bucket} rank {r}: {bad.size} differ, first {bad[0]}")
+        lay.close()
+
+
 def test_errors():
     numels = [10, 20]
     lay = zp.partition_layout(numels, 2, bucket=16)
