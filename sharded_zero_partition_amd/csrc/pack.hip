@@ -205,12 +205,8 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
     // then go through the scalar cache
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wave = int64_t(blockIdx.x) * (kPackThreads / 64) + wave_in_block;
-    if (a.hard.hard_per_b == 0) {
-        // in order: wave w takes span w
-        if (wave < a.n_span) pack_general<U>(a, wave * kSpan, lane);
-        return;
-    }
-    if (wave >= a.hard.n_hard) {
+    const bool in_order = a.hard.hard_per_b == 0;   // wave w takes span w
+    if (!in_order && wave >= a.hard.n_hard) {
         const int64_t w = wave - a.hard.n_hard;
         if (w >= a.n_span) return;   // the whole wave leaves together
         const int64_t o_wave = w * kSpan;
@@ -241,8 +237,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_span_kernel(const PackLaunc
             pack_general<U>(a, o_wave, lane);
         return;
     }
-    const int64_t w = hard_wave_span(wave, a.n_data_span, a.fill_base, a.hard, a.chunk_shift,
-                                     [&](int64_t i) { return i < a.n_src ? a.src[i].flat_off : a.psi; });
+    const int64_t w = in_order ? (wave < a.n_span ? wave : -1)
+                               : hard_wave_span(wave, a.n_data_span, a.fill_base, a.hard, a.chunk_shift,
+                                                [&](int64_t i) { return i < a.n_src ? a.src[i].flat_off : a.psi; });
     if (w < 0) return;
     pack_general<U>(a, w * kSpan, lane);
 }

@@ -626,14 +626,8 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
     const SpanGeometry geo = span_geometry(a.base, j_lo, j_hi, mis);
     bool bad = false;
 
-    if (a.hard.hard_per_b == 0) {
-        // in order: wave w takes span w
-        if (wave >= geo.n_span) return;
-        general_span<R, Epi>(a, geo.k_lo + wave * kSpanVec, geo.k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
-        Epi::finish(a, bad);
-        return;
-    }
-    if (wave >= a.hard.n_hard) {
+    const bool in_order = a.hard.hard_per_b == 0;   // wave w takes span w
+    if (!in_order && wave >= a.hard.n_hard) {
         // interior span w: whole and inside the range
         const int64_t w = wave - a.hard.n_hard;
         if (w < 1 || w >= geo.n_span - 1) return;   // the whole wave leaves together
@@ -672,8 +666,9 @@ __device__ __forceinline__ void owner_body(const typename Epi::Launch& a) {
         return;
     }
 
-    const int64_t w = hard_wave_span(wave, geo.n_span, geo.span0, a.hard, a.chunk_shift,
-                                     [&](int64_t i) { return a.off[i]; });
+    const int64_t w = in_order ? (wave < geo.n_span ? wave : -1)
+                               : hard_wave_span(wave, geo.n_span, geo.span0, a.hard, a.chunk_shift,
+                                                [&](int64_t i) { return a.off[i]; });
     if (w < 0) return;
     general_span<R, Epi>(a, geo.k_lo + w * kSpanVec, geo.k_end, mis, j_lo, j_hi, lane, wave_in_block, bad);
     Epi::finish(a, bad);
