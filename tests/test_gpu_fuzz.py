@@ -1,6 +1,7 @@
-"""Seeded random cases of the shard step against the oracle, the loss-scale
-growth rule on the GPU, and two host threads stepping different shards on
-their own streams at the same time."""
+"""Seeded random cases of the shard step against the oracle, of the pack and
+the reduce-to-owner over random tensor streams, the loss-scale growth rule on
+the GPU, and two host threads stepping different shards on their own streams
+at the same time."""
 
 import threading
 
@@ -10,7 +11,8 @@ import torch
 
 import oracle
 import sharded_zero_partition_amd as zp
-from gpu_harness import Lockstep, host_contribs
+from oracle import layout as OL
+from gpu_harness import Lockstep, host_contribs, margin_numels
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +39,85 @@ def test_random_cases():
             ls.step(c)
         ls.check_sentinels()
         assert ls.bit_exact, case
+
+
+def _views(rng, numels, scale=100.0):
+    """Device tensors carved from one buffer at random 2-byte offsets (every
+    alignment phase), fp16 values of moderate size."""
+    gaps = rng.integers(0, 9, size=len(numels))
+    total = int(sum(numels) + gaps.sum() + 8)
+    vals = (rng.standard_normal(total, dtype=np.float32) * np.float32(scale)).astype(np.float16)
+    buf = torch.from_numpy(vals.view(np.int16)).cuda()
+    out, off = [], 0
+    for n, g in zip(numels, gaps):
+        off += int(g)
+        out.append(buf[off:off + n])
+        off += n
+    return out
+
+
+def test_span_kernels_random_layouts():
+    """30 seeded random streams (mixes of empty, tiny, span- and chunk-sized
+    and long tensors, half of them with boundaries at the work order's
+    decision offsets), rank counts, alignments, bucket sizes and R: every fill
+    of the pack and every fill and owner of the reduce-to-owner (shard bases
+    at random misalignments) against the oracle, bit for bit."""
+    rng = np.random.default_rng(4242)
+    sent = 0x6B6B
+    for case in range(30):
+        if case % 2:
+            psi = int(rng.integers(3000, 120000))
+            numels = margin_numels(rng, [0], psi)
+        else:
+            numels = []
+            for _ in range(int(rng.integers(1, 120))):
+                kind = int(rng.integers(0, 5))
+                numels.append(int([0, rng.integers(1, 10), rng.integers(1000, 3000),
+                                   2048 * int(rng.integers(1, 4)), rng.integers(1, 30000)][kind]))
+            if sum(numels) == 0:
+                numels.append(17)
+        psi = sum(numels)
+        n_ranks = int(rng.integers(1, 7))
+        align = int(rng.choice([1, 8, 64]))
+        bucket = int(rng.choice([1000, 1024, 4093, 8192, 20487, psi]))
+        R = int(rng.integers(1, 9))
+        print(f"[span fuzz] case {case}: tensors {len(numels)} psi {psi} ranks {n_ranks} align {align} "
+              f"bucket {bucket} R {R}", flush=True)
+        lay = zp.partition_layout(numels, n_ranks, stage=2, align=align, bucket=bucket)
+        olay = OL.partition_layout(numels, n_ranks, 2, align, bucket)
+        # pack
+        tensors = _views(rng, numels)
+        lay.bind_tensors(tensors)
+        host_t = [t.cpu().numpy().view(np.uint16) for t in tensors]
+        b = torch.full((bucket,), sent, dtype=torch.int16, device="cuda")
+        for k in range(olay.n_fills):
+            lay.pack_bucket(k, b)
+            got = b.cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, oracle.pack_fill(host_t, k, bucket)), (case, k)
+        # reduce-to-owner
+        lists = [_views(rng, numels) for _ in range(R)]
+        lay.bind_contributions(lists)
+        host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+        S = olay.shard
+        for r in range(n_ranks):
+            mis = int(rng.integers(0, 8))
+            holder = torch.full((S + 16,), sent, dtype=torch.int16, device="cuda")
+            shard = holder[mis:mis + S]
+            want = np.full(S, sent, np.uint16)
+            for k in range(olay.n_fills):
+                n = lay.reduce_to_owner(k, r, shard)
+                off, vals = oracle.reduce_to_owner(host, olay, k, r)
+                assert n == vals.size
+                want[off:off + vals.size] = vals
+            got = shard.cpu().numpy().view(np.uint16)
+            # a NaN sum's payload bits are not specified: compare NaN-ness there
+            nan_w = ((want & 0x7C00) == 0x7C00) & ((want & 0x3FF) != 0)
+            nan_g = ((got & 0x7C00) == 0x7C00) & ((got & 0x3FF) != 0)
+            assert np.array_equal(nan_w, nan_g), (case, r)
+            assert np.array_equal(got[~nan_w], want[~nan_w]), (case, r, int(np.flatnonzero(got != want)[0]))
+            h = holder.cpu().numpy().view(np.uint16)
+            assert (h[:mis] == sent).all() and (h[mis + S:] == sent).all()
+        lay.close()
 
 
 def test_loss_scale_growth_matches_oracle():
