@@ -21,6 +21,9 @@
 // the loads of all U vectors before any is used; vectors that straddle
 // tensors, touch a tensor edge or the end of the stream are gathered element
 // by element.  No LDS staging: each wave's accesses are already contiguous.
+// The first waves of a launch take the spans near tensor boundaries and the
+// two ends of the fill's data (the work order of zp_internal.hpp), so that
+// their slower path does not hold up the launch's end.
 #include <hip/hip_ext.h>
 
 #include "vec16.hpp"

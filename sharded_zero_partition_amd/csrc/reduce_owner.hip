@@ -14,16 +14,20 @@
 //
 // Layout of the work: the owner's shard is cut into 8-element vectors on its
 // own 16-byte grid, so every full vector is one aligned 128-bit store.  A wave
-// owns 2 x 64 consecutive vectors (two 1 KiB store groups).  It reads the
-// source range of its span from the chunk index built at bind time; when the
-// span lies inside one tensor the tensor's offset, length and R addresses are
+// owns 2 x 64 consecutive vectors (two 1 KiB store groups).  The first waves
+// of a launch take the spans near tensor boundaries and the range's two ends
+// (the work order of zp_internal.hpp), so that their slower path does not
+// hold up the launch's end; every other wave reads one per-chunk record and
+// either finds its span inside that record's tensor or leaves.  In a span
+// inside one tensor the tensor's offset, length and R addresses are
 // wave-uniform (scalar loads), and so is each contribution's misalignment
 // phase: every lane then loads one aligned block per vector group and takes
 // the following block from its neighbour lane by cross-lane shuffle.
-// Otherwise, for each vector whose 8 elements lie in one tensor, each
-// contribution is read as aligned 16-byte blocks (funnel-shifted when
-// misaligned); vectors at the range ends or across tensor boundaries go
-// element by element.  HBM bytes per element: 2R read + 2 written.
+// Otherwise the span's candidate tensors are staged in LDS; a vector whose 8
+// elements lie in one tensor reads each contribution as aligned 16-byte
+// blocks (funnel-shifted when misaligned), and vectors at the range ends or
+// across tensor boundaries gather element by element.  HBM bytes per
+// element: 2R read + 2 written.
 //
 // The owner step runs the same walk over the owner's whole real range and,
 // in place of the fp16 store, the shard step's arithmetic (adam.hpp): the
