@@ -118,9 +118,12 @@ __device__ __forceinline__ void finish_pass(const StepLaunch& a, bool bad) {
 // covering [1024 t, 1024 (t+1)), and the grid holds one wave per tile.  Lane
 // l holds elements 4l..4l+3 of each group, so every load and store
 // instruction of the wave touches one contiguous 1 KiB (fp32) or 512 B (fp16)
-// range.  A wave issues all of its tile's loads, computes, stores and ends;
-// the hardware keeps several such waves per SIMD in flight (77 VGPRs at
-// R = 2, 148 at R = 16) and hands each free slot the next tile.  On the same
+// range.  A wave loads its tile, computes, stores and ends (at R = 2 the
+// compiler issues the contributions and the first two groups' p, m, v, and
+// the last two groups' after the first groups' arithmetic, which keeps the
+// kernel at 77 VGPRs; forcing every load first took 88 VGPRs and ran 1%
+// slower); the hardware keeps several such waves per SIMD in flight (148
+// VGPRs at R = 16) and hands each free slot the next tile.  On the same
 // buffers this ran 3-6% faster for every R than a persistent grid (one block
 // per CU) whose waves walked their tiles with a register double buffer, with
 // the same results bit for bit; 512- and 2048-element tiles ran slower.
