@@ -346,7 +346,8 @@ int zero_shard_step(zero_shard_state* st, const uint16_t* const* grads, int32_t 
  * What differs: the flag word, the blocks-done counter and the decision word
  * live in a fixed 256-byte device array of the library (one copy per device
  * and process, kept until the process ends) instead of a workspace allocated
- * on a device's first call, and the call clears those words on `stream`,
+ * on a device's first call, and the call clears those words on `stream`
+ * (with a one-block kernel),
  * copies the 8-byte decision back into host memory after the pass and waits
  * for `stream` (zero_shard_step instead polls a pinned host word).  The array
  * keeps the last call's contents; calls on one device are serialised by the

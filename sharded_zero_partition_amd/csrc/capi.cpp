@@ -161,6 +161,7 @@ int get_workspace(int dev, DeviceWorkspace** out) {
         if (!ws) return fail(ZERO_ERR_OUT_OF_MEMORY, "workspace allocation failed");
         hipError_t e = hipDeviceGetAttribute(&ws->cu_count, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+        static_assert(kStaticScratchWords * sizeof(uint32_t) == 256, "clear_scratch zeroes the whole workspace");
         e = hipMalloc(reinterpret_cast<void**>(&ws->d_flag), 256);
         if (e != hipSuccess) return fail_hip(e, "hipMalloc (flag)");
         e = hipMemset(ws->d_flag, 0, 256);
@@ -288,8 +289,9 @@ int begin_step(void* stream, const char* who, DeviceWorkspace** ws, std::unique_
     if (rc != ZERO_OK) return rc;
     *lock = std::unique_lock<std::mutex>((*ws)->mu);
     if (++(*ws)->epoch == 0) {
-        e = hipMemsetAsync((*ws)->d_flag, 0, sizeof(uint32_t), static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync (flag)");
+        // the workspace is 256 bytes, the size clear_scratch zeroes
+        e = clear_scratch((*ws)->d_flag, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, "clearing the flag word");
         __atomic_store_n((*ws)->h_word, 0ull, __ATOMIC_RELEASE);
         (*ws)->epoch = 1;
     }
@@ -470,8 +472,8 @@ extern "C" int zero_shard_step_noalloc(zero_shard_state* st, const uint16_t* con
         std::lock_guard<std::mutex> lock(zp::g_noalloc_mu[dev]);
         hipStream_t s = static_cast<hipStream_t>(stream);
         // the flag, the counter and the decision word start at 0
-        e = hipMemsetAsync(w, 0, zp::kStaticScratchWords * sizeof(uint32_t), s);
-        if (e != hipSuccess) return zp::fail_hip(e, "hipMemsetAsync (scratch)");
+        e = zp::clear_scratch(w, s);
+        if (e != hipSuccess) return zp::fail_hip(e, "clearing the scratch words");
 
         zp::StepLaunch a;
         std::memset(&a, 0, sizeof(a));

@@ -23,6 +23,19 @@ std::mutex g_scratch_mu;
 uint32_t* g_scratch_ptr[kMaxScratchDevices] = {};
 }  // namespace
 
+namespace {
+// Zeroes n words at w (one block; n <= 64 * 4).  A kernel rather than a
+// memset node, so the clear is an ordinary launch on the caller's stream.
+__global__ void clear_words_kernel(uint32_t* w, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) w[i] = 0u;
+}
+}  // namespace
+
+hipError_t clear_scratch(uint32_t* w, hipStream_t stream) {
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, stream, w, kStaticScratchWords);
+    return hipGetLastError();
+}
+
 int static_scratch(int dev, uint32_t** out) {
     if (dev < 0 || dev >= kMaxScratchDevices) return fail(ZERO_ERR_INVALID_ARG, "device index out of range");
     std::lock_guard<std::mutex> lock(g_scratch_mu);

@@ -301,5 +301,7 @@ int blocks_per_cu_step();
 // of it (looked up once per device, with `dev` the current device).
 constexpr int kStaticScratchWords = 64;
 int static_scratch(int dev, uint32_t** out);
+// Zeroes the kStaticScratchWords words at w on `stream` with a one-block kernel.
+hipError_t clear_scratch(uint32_t* w, hipStream_t stream);
 
 }  // namespace zp

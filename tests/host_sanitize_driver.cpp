@@ -44,6 +44,7 @@ int static_scratch(int, uint32_t**) {
     (void)never("static scratch");
     return -1;
 }
+hipError_t clear_scratch(uint32_t*, hipStream_t) { return never("clear scratch"); }
 }  // namespace zp
 
 extern "C" {
