@@ -40,6 +40,9 @@
 // host.
 #include <hip/hip_ext.h>
 
+#include <array>
+#include <utility>
+
 #include "adam.hpp"
 #include "vec16.hpp"
 #include "zp_internal.hpp"
@@ -712,6 +715,18 @@ __global__ void publish_flag_kernel(const uint32_t* flag, uint32_t epoch, unsign
     __hip_atomic_store(host_word, word, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// The kernels for R = 1..16, indexed by R - 1.
+template <int... I>
+std::array<void (*)(ReduceLaunch), sizeof...(I)> reduce_kernels(std::integer_sequence<int, I...>) {
+    return {{&reduce_owner_kernel<I + 1>...}};
+}
+template <int... I>
+std::array<void (*)(OwnerLaunch), sizeof...(I)> owner_kernels(std::integer_sequence<int, I...>) {
+    return {{&owner_step_kernel<I + 1>...}};
+}
+const auto kReduceKernels = reduce_kernels(std::make_integer_sequence<int, kMaxReduceRanks>{});
+const auto kOwnerKernels = owner_kernels(std::make_integer_sequence<int, kMaxReduceRanks>{});
+
 // Workgroups of the launch plan: n_hard waves, then one wave per span.
 dim3 plan_grid(const ReduceLaunch& a) {
     const int64_t waves = a.hard.n_hard + a.n_span;   // <= kMaxGridWaves (checked by the launchers)
@@ -725,24 +740,8 @@ dim3 plan_grid(const ReduceLaunch& a) {
 hipError_t launch_reduce_owner(const ReduceLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     if (a.hard.n_hard + a.n_span > kMaxGridWaves) return hipErrorInvalidConfiguration;
     const dim3 grid = plan_grid(a);
-    switch (a.R) {
-        case 1: hipExtLaunchKernelGGL(reduce_owner_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 2: hipExtLaunchKernelGGL(reduce_owner_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 3: hipExtLaunchKernelGGL(reduce_owner_kernel<3>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 4: hipExtLaunchKernelGGL(reduce_owner_kernel<4>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 5: hipExtLaunchKernelGGL(reduce_owner_kernel<5>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 6: hipExtLaunchKernelGGL(reduce_owner_kernel<6>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 7: hipExtLaunchKernelGGL(reduce_owner_kernel<7>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 8: hipExtLaunchKernelGGL(reduce_owner_kernel<8>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 9: hipExtLaunchKernelGGL(reduce_owner_kernel<9>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 10: hipExtLaunchKernelGGL(reduce_owner_kernel<10>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 11: hipExtLaunchKernelGGL(reduce_owner_kernel<11>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 12: hipExtLaunchKernelGGL(reduce_owner_kernel<12>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 13: hipExtLaunchKernelGGL(reduce_owner_kernel<13>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 14: hipExtLaunchKernelGGL(reduce_owner_kernel<14>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 15: hipExtLaunchKernelGGL(reduce_owner_kernel<15>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        default: hipExtLaunchKernelGGL(reduce_owner_kernel<16>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-    }
+    if (a.R < 1 || a.R > kMaxReduceRanks) return hipErrorInvalidValue;   // checked at bind time
+    hipExtLaunchKernelGGL(kReduceKernels[a.R - 1], grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -751,30 +750,14 @@ namespace {
 // The owner step's main pass over the real elements [g_lo, g_hi).
 void launch_owner_real(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     const dim3 grid = plan_grid(a);
-    switch (a.R) {
-        case 1: hipExtLaunchKernelGGL(owner_step_kernel<1>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 2: hipExtLaunchKernelGGL(owner_step_kernel<2>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 3: hipExtLaunchKernelGGL(owner_step_kernel<3>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 4: hipExtLaunchKernelGGL(owner_step_kernel<4>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 5: hipExtLaunchKernelGGL(owner_step_kernel<5>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 6: hipExtLaunchKernelGGL(owner_step_kernel<6>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 7: hipExtLaunchKernelGGL(owner_step_kernel<7>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 8: hipExtLaunchKernelGGL(owner_step_kernel<8>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 9: hipExtLaunchKernelGGL(owner_step_kernel<9>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 10: hipExtLaunchKernelGGL(owner_step_kernel<10>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 11: hipExtLaunchKernelGGL(owner_step_kernel<11>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 12: hipExtLaunchKernelGGL(owner_step_kernel<12>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 13: hipExtLaunchKernelGGL(owner_step_kernel<13>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 14: hipExtLaunchKernelGGL(owner_step_kernel<14>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        case 15: hipExtLaunchKernelGGL(owner_step_kernel<15>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-        default: hipExtLaunchKernelGGL(owner_step_kernel<16>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a); break;
-    }
+    hipExtLaunchKernelGGL(kOwnerKernels[a.R - 1], grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a);
 }
 
 }  // namespace
 
 hipError_t launch_owner_step(const OwnerLaunch& a, hipStream_t stream, const KernelEvents& ev) {
     if (a.hard.n_hard + a.n_span > kMaxGridWaves) return hipErrorInvalidConfiguration;
+    if (a.R < 1 || a.R > kMaxReduceRanks) return hipErrorInvalidValue;   // checked at bind time
     // the shard is [0, a.st.n): its real elements first, then its padding
     const int64_t n_real = a.g_hi - a.g_lo;
     const bool pad = a.st.n > n_real;
