@@ -11,10 +11,13 @@ misaligned tensors, every rank, R = 1..16, several steps with new gradient
 values each; inf/NaN inside and outside the owner's range; a rank that holds
 only padding; zero padding staying zero over NaN-filled alternates and a
 following shard step; the fused shard step on the same sums (cross-check of
-the two kernels); argument errors; and, sampled, the 13B model's rank 63 as
-the benchmark runs it and the 20,000-tensor stream's first and last owner."""
+the two kernels); argument errors; the 13B model's rank 63 as the benchmark
+runs it, every element of the shard; and, sampled, a shard past index 2^31
+and the 20,000-tensor stream's first and last owner."""
 
 import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -531,26 +534,111 @@ def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1
     return flags
 
 
-def test_13b_rank63_sampled():
+def _window(buf, starts, offs, lo, hi):
+    """The stream's elements of flat indices [lo, hi), gathered tensor piece by
+    tensor piece on the device, as host fp16 bit patterns."""
+    first = int(np.searchsorted(offs, lo, side="right") - 1)
+    pieces, g = [], lo
+    for ti in range(first, len(offs) - 1):
+        if g >= hi:
+            break
+        a, b = g, min(hi, int(offs[ti + 1]))
+        if b > a:
+            s0 = int(starts[ti] + a - offs[ti])
+            pieces.append(buf[s0:s0 + (b - a)])
+        g = b
+    return torch.cat(pieces).cpu().numpy().view(np.uint16) if pieces else np.zeros(0, np.uint16)
+
+
+def _whole_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, plant=None):
+    """As _sampled_owner_steps, but every element of the rank's shard is
+    compared: the oracle's shard step runs over the whole shard in
+    contiguous chunks on the host's threads (its C calls release the GIL;
+    each element depends only on its own inputs and the shard-wide flag,
+    which is the expected one), on the rank's windows of the R streams,
+    zero over the padding.  Returns the flags."""
+    psi = int(sum(numels))
+    lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=1 << 26)
+    S = lay.info.shard_elems
+    lo = rank * S
+    n = max(0, min(lo + S, psi) - lo)
+    offs = np.concatenate([[0], np.cumsum(np.asarray(numels, np.int64))])
+    p0 = W.normal_f32(S, 0.02, wid, W.KIND_MASTER, 0, rank, "cuda")
+    p0[n:] = 0
+    st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0),
+                       torch.empty_like(p0), torch.empty_like(p0), torch.empty_like(p0))
+    slot = torch.empty(S, dtype=torch.int16, device="cuda")
+    ost = oracle.ShardState(p0.cpu().numpy())
+    sc, osc = zp.LossScaler.make(scale), oracle.LossScaler(scale)
+    out16 = np.empty(S, np.uint16)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    cuts = np.linspace(0, S, threads * 4 + 1).astype(np.int64)
+    parts = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    print(f"[owner step, whole shard] psi={psi} ranks={n_ranks} rank={rank} S={S} n={n} R={R}", flush=True)
+    flags = []
+    for step in range(1, steps + 1):
+        streams = [W.gradient_stream(numels, wid, r, osc.scale, step, "cuda") for r in range(R)]
+        want_flag = 0
+        for r, g, bits in (plant or {}).get(step, []):
+            buf, starts, _ = streams[r]
+            ti = int(np.searchsorted(offs, g, side="right") - 1)
+            buf[int(starts[ti] + g - offs[ti])] = int(np.int16(np.uint16(bits)))
+            want_flag |= int(lo <= g < lo + n)
+        lay.bind_contributions([views for _, _, views in streams])
+        flag = lay.owner_step(rank, st, HPC, sc, slot)
+        torch.cuda.synchronize()
+        assert flag == want_flag, f"step {step}: flag {flag}, expected {want_flag}"
+        flags.append(flag)
+        contribs = []
+        for buf, starts, _ in streams:
+            c = np.zeros(S, np.uint16)                      # no gradient over the padding
+            c[:n] = _window(buf, starts, offs, lo, lo + n)
+            contribs.append(c)
+        del streams
+        used = osc.scale
+        if not want_flag:
+            def work(ab):
+                a, b = ab
+                oracle.adam_apply([c[a:b] for c in contribs], ost.p[a:b], ost.m[a:b], ost.v[a:b],
+                                  out16[a:b], used, ost.t + 1, HP)
+            with ThreadPoolExecutor(threads) as pool:
+                list(pool.map(work, parts))
+            ost.t += 1
+        else:
+            # a skipped step restores the slot to fp16 of the live master
+            out16[:] = oracle.float_to_half(ost.p)
+        osc.update(bool(want_flag))
+        assert st.t == ost.t and sc.scale == osc.scale
+        for name, got, want in zip("pmv", st.live(), (ost.p, ost.m, ost.v)):
+            gv = got.cpu().numpy()
+            bad = np.flatnonzero(gv.view(np.uint32) != want.view(np.uint32))
+            assert bad.size == 0, f"step {step} {name}: {bad.size} of {S} differ, first at {bad[0]}"
+        sv = slot.cpu().numpy().view(np.uint16)
+        bad = np.flatnonzero(sv != out16)
+        assert bad.size == 0, f"step {step} slot: {bad.size} differ, first at {bad[0]}"
+    lay.close()
+    return flags
+
+
+def test_13b_rank63_whole_shard():
     """The benchmark's owner-step configuration: the 13B model's 484 tensors
     (12.85e9 elements), N = 64, rank 63 (S = 200,752,240), R = 2 streams at
-    loss scale 1024, three steps."""
+    loss scale 1024, three steps; every element of the shard compared."""
     w = W.zero3_13b()
-    _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3)
+    _whole_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3)
 
 
-def test_13b_rank63_overflow_sampled():
+def test_13b_rank63_overflow_whole_shard():
     """The benchmark's owner-step configuration with an overflow: on step 2
     contribution 1 holds +inf at a position inside rank 63's range and
     contribution 0 a NaN outside it (rank 62's).  Flags 0, 1, 0; the skipped
     step leaves the state as it was and restores the whole slot to fp16 of
     the master; the loss scale halves and the next step runs at the new
-    scale.  Sampled against the oracle, the planted position included."""
+    scale.  Every element of the shard compared against the oracle."""
     w = W.zero3_13b()
     lo = w.rank * w.shard
     plant = {2: [(1, lo + 12_345_678, 0x7C00), (0, lo - 1000, 0x7E00)]}
-    flags = _sampled_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3,
-                                 n_sample=1 << 18, plant=plant)
+    flags = _whole_owner_steps(w.numels, w.n_ranks, w.rank, 2, w.wid, w.scale, 3, plant=plant)
     assert flags == [0, 1, 0]
 
 
