@@ -12,8 +12,8 @@ values each; inf/NaN inside and outside the owner's range; a rank that holds
 only padding; zero padding staying zero over NaN-filled alternates and a
 following shard step; the fused shard step on the same sums (cross-check of
 the two kernels); argument errors; the 13B model's rank 63 as the benchmark
-runs it, every element of the shard; and, sampled, a shard past index 2^31
-and the 20,000-tensor stream's first and last owner."""
+runs it and the 20,000-tensor stream's first and last owner, every element
+of the shard; and, sampled, a shard past index 2^31."""
 
 import ctypes
 import os
@@ -654,9 +654,9 @@ def test_shard_past_2_31_sampled():
 
 
 @pytest.mark.parametrize("rank", [0, 15])
-def test_pack_20k_stream_sampled(rank):
+def test_pack_20k_stream_whole_shard(rank):
     """The 20,000 log-uniform tensors (5.48e9 elements) cut for 16 owners:
     the first owner and the last (whose shard ends in 8 padding elements),
-    R = 2, one step."""
+    R = 2, one step; every element of the shard compared."""
     pw = W.pack_20k()
-    _sampled_owner_steps(pw.numels, pw.n_ranks, rank, 2, pw.wid, 1024.0, 1)
+    _whole_owner_steps(pw.numels, pw.n_ranks, rank, 2, pw.wid, 1024.0, 1)
