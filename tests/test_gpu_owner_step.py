@@ -12,8 +12,8 @@ values each; inf/NaN inside and outside the owner's range; a rank that holds
 only padding; zero padding staying zero over NaN-filled alternates and a
 following shard step; the fused shard step on the same sums (cross-check of
 the two kernels); argument errors; the 13B model's rank 63 as the benchmark
-runs it and the 20,000-tensor stream's first and last owner, every element
-of the shard; and, sampled, a shard past index 2^31."""
+runs it, the 20,000-tensor stream's first and last owner and a shard past
+index 2^31, every element of the shard."""
 
 import ctypes
 import os
@@ -455,84 +455,8 @@ def test_errors():
 
 
 # ---------------------------------------------------------------------------
-# full sizes, sampled
+# full sizes, every element
 # ---------------------------------------------------------------------------
-
-def _sampled_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, n_sample=1 << 20, plant=None):
-    """R whole gradient streams (workloads.gradient_stream), the owner step of
-    `rank` for `steps` steps with new streams each step, compared on a sample
-    of the rank's shard (both ends of its real range, every tensor boundary
-    inside it, one random element of every 1024-element tile, n_sample random
-    positions and all of its padding) against the
-    oracle's shard step over the sampled sums (zero over the padding).  The draws are finite and their
-    pairwise fp32 sums cannot overflow, so the overflow flag is 0 unless
-    `plant` ({step: [(contribution, flat index, fp16 bits)]}) puts a special
-    value inside the rank's range on that step; planted positions inside the
-    range are part of the sample.  Returns the flags."""
-    psi = int(sum(numels))
-    lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=1 << 26)
-    S = lay.info.shard_elems
-    lo = rank * S
-    n = max(0, min(lo + S, psi) - lo)
-    offs = np.concatenate([[0], np.cumsum(np.asarray(numels, np.int64))])
-    rng = np.random.default_rng(wid * 100 + rank)
-    inner = offs[(offs > lo) & (offs < lo + n)] - lo
-    planted = [g - lo for v in (plant or {}).values() for _, g, _ in v if lo <= g < lo + n]
-    tiles = np.arange(0, n, 1024, dtype=np.int64)           # one element of every 1024-element tile
-    pick = np.concatenate([np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n),
-                           inner, inner - 1, rng.integers(0, max(n, 1), size=n_sample),
-                           np.asarray(planted, np.int64), np.arange(n, S),
-                           tiles + rng.integers(0, 1024, size=tiles.size)])
-    sample = np.unique(pick[(pick >= 0) & (pick < S)]).astype(np.int64)
-    real = sample < n
-    g = sample[real] + lo
-    tens = np.searchsorted(offs, g, side="right") - 1
-    rel = g - offs[tens]
-    p0 = W.normal_f32(S, 0.02, wid, W.KIND_MASTER, 0, rank, "cuda")
-    p0[n:] = 0
-    st = zp.ShardState(p0, torch.zeros_like(p0), torch.zeros_like(p0),
-                       torch.empty_like(p0), torch.empty_like(p0), torch.empty_like(p0))
-    slot = torch.empty(S, dtype=torch.int16, device="cuda")
-    idx = torch.from_numpy(sample).cuda()
-    ost = oracle.ShardState(p0[idx].cpu().numpy())
-    sc, osc = zp.LossScaler.make(scale), oracle.LossScaler(scale)
-    print(f"[owner step] psi={psi} ranks={n_ranks} rank={rank} S={S} n={n} R={R} "
-          f"sample={sample.size}", flush=True)
-    flags = []
-    out16 = np.empty(sample.size, np.uint16)
-    for step in range(1, steps + 1):
-        streams = [W.gradient_stream(numels, wid, r, osc.scale, step, "cuda") for r in range(R)]
-        want_flag = 0
-        for r, g, bits in (plant or {}).get(step, []):
-            buf, starts, _ = streams[r]
-            ti = int(np.searchsorted(offs, g, side="right") - 1)
-            buf[int(starts[ti] + g - offs[ti])] = int(np.int16(np.uint16(bits)))
-            want_flag |= int(lo <= g < lo + n)
-        lay.bind_contributions([views for _, _, views in streams])
-        flag = lay.owner_step(rank, st, HPC, sc, slot)
-        torch.cuda.synchronize()
-        assert flag == want_flag, f"step {step}: flag {flag}, expected {want_flag}"
-        flags.append(flag)
-        contribs = []
-        for buf, starts, _ in streams:
-            pos = torch.from_numpy(starts[tens] + rel).cuda()
-            c = np.zeros(sample.size, np.uint16)            # no gradient over the padding
-            c[real] = buf[pos].cpu().numpy().view(np.uint16)
-            contribs.append(c)
-        oracle.shard_step(ost, contribs, osc, HP, out16, flag=want_flag)
-        if want_flag:
-            # a skipped step restores the slot to fp16 of the live master
-            out16[:] = oracle.float_to_half(ost.p)
-        del streams
-        assert st.t == ost.t and sc.scale == osc.scale
-        for name, got, want in zip("pmv", st.live(), (ost.p, ost.m, ost.v)):
-            gv = got[idx].cpu().numpy()
-            bad = np.flatnonzero(gv.view(np.uint32) != want.view(np.uint32))
-            assert bad.size == 0, f"step {step} {name}: {bad.size} differ, first at {sample[bad[0]]}"
-        assert np.array_equal(slot[idx].cpu().numpy().view(np.uint16), out16), f"step {step} slot"
-    lay.close()
-    return flags
-
 
 def _window(buf, starts, offs, lo, hi):
     """The stream's elements of flat indices [lo, hi), gathered tensor piece by
@@ -551,12 +475,17 @@ def _window(buf, starts, offs, lo, hi):
 
 
 def _whole_owner_steps(numels, n_ranks, rank, R, wid, scale, steps, plant=None):
-    """As _sampled_owner_steps, but every element of the rank's shard is
-    compared: the oracle's shard step runs over the whole shard in
+    """R whole gradient streams (workloads.gradient_stream), the owner step of
+    `rank` for `steps` steps with new streams each step, and every element of
+    the rank's shard (master, momentum, variance, slot) compared bit for bit
+    against the oracle's shard step on the rank's windows of the streams,
+    zero over the padding.  The oracle runs over the whole shard in
     contiguous chunks on the host's threads (its C calls release the GIL;
     each element depends only on its own inputs and the shard-wide flag,
-    which is the expected one), on the rank's windows of the R streams,
-    zero over the padding.  Returns the flags."""
+    which is the expected one).  The draws are finite and their pairwise
+    fp32 sums cannot overflow, so the overflow flag is 0 unless `plant`
+    ({step: [(contribution, flat index, fp16 bits)]}) puts a special value
+    inside the rank's range on that step.  Returns the flags."""
     psi = int(sum(numels))
     lay = zp.partition_layout(numels, n_ranks, stage=2, bucket=1 << 26)
     S = lay.info.shard_elems
@@ -642,14 +571,14 @@ def test_13b_rank63_overflow_whole_shard():
     assert flags == [0, 1, 0]
 
 
-def test_shard_past_2_31_sampled():
+def test_shard_past_2_31_whole_shard():
     """Element indices past the signed 32-bit range: rank 1 of 2 over three
     tensors of 2^32 + 8198 elements in all, so its shard (2^31 + 4099
     elements) starts past flat index 2^31, reaches past 2^32 and holds a
-    tensor boundary; R = 2 streams, two steps."""
+    tensor boundary; R = 2 streams, two steps; every element compared."""
     numels = [(1 << 31) + 4096, (1 << 31) - 7, 4109]
     torch.cuda.empty_cache()
-    _sampled_owner_steps(numels, 2, 1, 2, W.past_2_31().wid, 1024.0, 2, n_sample=1 << 18)
+    _whole_owner_steps(numels, 2, 1, 2, W.past_2_31().wid, 1024.0, 2)
     torch.cuda.empty_cache()
 
 
