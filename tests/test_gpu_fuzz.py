@@ -1,7 +1,8 @@
 """Seeded random cases of the shard step against the oracle, of the pack and
 the reduce-to-owner over random tensor streams, the loss-scale growth rule on
-the GPU, and two host threads stepping different shards on their own streams
-at the same time."""
+the GPU, two host threads stepping different shards on their own streams at
+the same time, and two host threads packing and reducing on their own
+layouts and streams at the same time."""
 
 import threading
 
@@ -166,3 +167,66 @@ def test_two_threads_two_streams():
     assert not errors, errors
     for r in runs:
         assert r.ts == [1, 2, 3, 4] and r.bit_exact
+
+
+def test_two_threads_pack_and_reduce():
+    """Two host threads, each with its own layout and stream, pack and reduce
+    to owner at the same time (the launch planning and kernel timing are
+    per call and per thread); every fill and owner against the oracle."""
+    rng = np.random.default_rng(10)
+    cases = []
+    for k in range(2):
+        numels = [int(x) for x in rng.choice([1, 7, 300, 2049, 5000, 40000], size=60)]
+        bucket = [4093, 20487][k]
+        lay = zp.partition_layout(numels, 3, stage=2, align=8, bucket=bucket)
+        olay = OL.partition_layout(numels, 3, 2, 8, bucket)
+        tensors = _views(rng, numels)
+        lists = [_views(rng, numels) for _ in range(2)]
+        cases.append((numels, bucket, lay, olay, tensors, lists))
+    results = [None, None]
+    errors = []
+
+    def work(k):
+        try:
+            torch.cuda.set_device(0)
+            numels, bucket, lay, olay, tensors, lists = cases[k]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                lay.bind_tensors(tensors, stream=s)
+                lay.bind_contributions(lists, stream=s)
+                fills = []
+                b = torch.empty(bucket, dtype=torch.int16, device="cuda")
+                for f in range(olay.n_fills):
+                    lay.pack_bucket(f, b, stream=s)
+                    fills.append(b.clone())
+                S = olay.shard
+                flat = torch.full((3 * S,), 0x6B6B, dtype=torch.int16, device="cuda")
+                for f in range(olay.n_fills):
+                    for r in range(3):
+                        lay.reduce_to_owner(f, r, flat[r * S:(r + 1) * S], stream=s)
+                s.synchronize()
+                results[k] = ([x.cpu().numpy().view(np.uint16) for x in fills], flat.cpu().numpy().view(np.uint16))
+        except Exception as e:        # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k in range(2):
+        numels, bucket, lay, olay, tensors, lists = cases[k]
+        fills, flat = results[k]
+        host_t = [t.cpu().numpy().view(np.uint16) for t in tensors]
+        for f in range(olay.n_fills):
+            assert np.array_equal(fills[f], oracle.pack_fill(host_t, f, bucket)), (k, f)
+        host = [[t.cpu().numpy().view(np.uint16) for t in lst] for lst in lists]
+        S = olay.shard
+        for r in range(3):
+            want = np.full(S, 0x6B6B, np.uint16)
+            for f in range(olay.n_fills):
+                off, vals = oracle.reduce_to_owner(host, olay, f, r)
+                want[off:off + vals.size] = vals
+            assert np.array_equal(flat[r * S:(r + 1) * S], want), (k, r)
+        lay.close()
