@@ -183,6 +183,7 @@ def test_two_threads_pack_and_reduce():
         tensors = _views(rng, numels)
         lists = [_views(rng, numels) for _ in range(2)]
         cases.append((numels, bucket, lay, olay, tensors, lists))
+    torch.cuda.synchronize()   # the set-up copies are done before the threads' streams start
     results = [None, None]
     errors = []
 

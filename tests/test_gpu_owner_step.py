@@ -168,6 +168,48 @@ def test_dense_boundaries_run_in_order(R):
     lay.close()
 
 
+def test_two_threads_owner_steps():
+    """Two host threads on their own streams, each running owner steps for
+    both ranks of its own layout, each step checked against the oracle in the
+    thread; the library serialises the steps of one device."""
+    import threading
+    rng = np.random.default_rng(960)
+    jobs = []
+    for k in range(2):
+        numels = [int(x) for x in rng.choice([1, 9, 300, 2049, 5000, 30000], size=40)]
+        lay = zp.partition_layout(numels, 2, stage=2, align=8, bucket=4096)
+        olay = OL.partition_layout(numels, 2, 2, 8, 4096)
+        bufs, lists = _lists(rng, numels, 2)
+        lay.bind_contributions(lists)
+        runs = [OwnerRun(olay, r, rng, slot_offset=int(rng.integers(0, 8))) for r in range(2)]
+        jobs.append((lay, lists, runs))
+    torch.cuda.synchronize()   # the set-up copies are done before the threads' streams start
+    errors = []
+
+    def work(k):
+        try:
+            torch.cuda.set_device(0)
+            lay, lists, runs = jobs[k]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                host = _host(lists)
+                for _ in range(3):
+                    for r, run in enumerate(runs):
+                        assert run.step(lay, r, host) == 0
+        except Exception as e:        # reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for lay, _, runs in jobs:
+        assert all(run.state.t == 3 for run in runs)
+        lay.close()
+
+
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 7, 9, 16])
 def test_small_ragged_layouts_every_rank(R):
     rng = np.random.default_rng(500 + R)
